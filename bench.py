@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert NVFP4 W4A4 MoE layer on one MI355X.
+
+One step = one pass of the whole layer over one batch of seeded synthetic
+tokens: sigmoid+bias top-k routing and the expert permutation, NVFP4
+quantization of the activations, gate_up + SwiGLU + re-quantization, down +
+weighted scatter with the per-pair sum of squares, the combine, and the REAP
+saliency finalize.  Inputs are resident in HBM before the timed region.
+
+Default workload: the decode-shaped layer (80 experts, top-8, hidden 6144,
+intermediate 2048, 16 tokens), HBM-bound.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed-MoE layer tokens/sec (NVFP4 W4A4) + % HBM / % MFMA roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+FFN_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_mixture_amd", "csrc", "ffn.hip")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = decode-shaped layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the oracle's timed sample")
+    return ap.parse_args(argv)
+
+
+def ffn_source_hash() -> str:
+    with open(FFN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stage_bytes_flops(cfg, counts):
+    """Algorithmic bytes and FLOPs of the two FFN stages for one launch."""
+    import numpy as np
+
+    H, I, T, k = cfg.H, cfg.I, cfg.T, cfg.k
+    touched = int(np.count_nonzero(counts))
+    pairs = T * k
+    nv = 0.5625  # bytes per NVFP4 element: 4-bit code + one E4M3 byte per 16
+    w13 = 2 * I * H * nv
+    w2 = H * I * nv
+    gate_up_bytes = touched * w13 + T * H * nv + pairs * I * nv  # weights + x codes + h codes out
+    down_bytes = touched * w2 + pairs * I * nv + pairs * H * 4  # weights + h codes + pair_out (fp32)
+    return dict(touched=touched,
+                gate_up=dict(bytes=gate_up_bytes, flops=2.0 * pairs * H * 2 * I, per_expert_bytes=w13),
+                down=dict(bytes=down_bytes, flops=2.0 * pairs * I * H, per_expert_bytes=w2))
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it matches the current kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    h = re.search(r"ffn_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not h or h.group(1) != ffn_source_hash():
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(cfg, n_tokens: int) -> dict:
+    """The oracle on a bounded sample of the same workload (the first n_tokens tokens)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import moe as omoe
+    from oracle import routing as oroute
+    from workloads import gen
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    ws = cfg.weights
+    rows = list(range(n_tokens))
+    x = gen.token_rows(cfg, rows)
+    wr = gen.router_weight(ws)
+    bias = gen.router_bias(cfg)
+    gs_x, gs_h = gen.global_scales(ws)
+    # offline part (not timed): which experts the sample needs, and their RTN weights
+    ids, _, _, _ = oroute.route(x, wr, bias, cfg.k, cfg.rsf)
+    need = sorted(set(int(e) for e in ids.reshape(-1)))
+    experts = {}
+
+    def ptq(item):
+        e, g, u, d = item
+        f32 = gen.bf16_bits_to_f32
+        return e, omoe.quantize_expert(f32(g), f32(u), f32(d))
+
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        for e, q in ex.map(ptq, gen.iter_experts_bf16(ws, need)):
+            experts[e] = q
+    t0 = time.perf_counter()
+    out = omoe.moe_layer(x, wr, bias, cfg.k, cfg.rsf, gs_x, lambda e: experts[e], gs_h)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(out["y"]).all()
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except Exception:  # pragma: no cover
+        pass
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the same batch ({len(need)} experts touched), full layer incl. "
+                      f"routing, quantization, fp64 expert FFN over dequantized operands, combine and REAP; "
+                      f"{dt:.2f} s; offline RTN of the weights not timed; host CPU: {cpu}"}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this layer build runs on exactly one GPU; --gpus must be 1 "
+                                   "(multi-GPU expert sharding is described in DESIGN.md, not built)"}), flush=True)
+        return 2
+    import numpy as np
+    import torch
+
+    from nvfp4_w4a4_mixture_amd import workload_io
+    from workloads import CONFIGS
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    layer, _ = workload_io.build_layer(cfg, dev)
+    x = workload_io.tokens(cfg, dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    stages = layer.STAGES
+
+    for _ in range(args.warmup):
+        layer(x, out_dtype=torch.bfloat16, reap=True)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        out = layer(x, out_dtype=torch.bfloat16, reap=True, events=events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = t1 - t0
+    ms_stage = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j, s in enumerate(stages)}
+    counts = out.route.expert_counts.cpu().numpy()
+    bf = stage_bytes_flops(cfg, counts)
+    dom = "gate_up" if ms_stage["gate_up"] >= ms_stage["down"] else "down"
+    dom_s = ms_stage[dom] / 1e3
+    workload = cfg.name
+    kernel = {"gate_up": "ffn_gate_up", "down": "ffn_down"}[dom]
+    if cfg.bound == "mfma":
+        achieved = bf[dom]["flops"] / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS}
+    else:
+        achieved = bf[dom]["bytes"] / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof["traffic"] = read_traffic(kernel, workload)
+    roof["kernel"] = kernel
+    roof["kernel_ms"] = ms_stage[dom]
+    roof["algorithmic_bytes"] = bf[dom]["bytes"]
+    roof["algorithmic_flops"] = bf[dom]["flops"]
+    # the whole FFN (both stages) against the same roofline, for context
+    ffn_s = (ms_stage["gate_up"] + ms_stage["down"]) / 1e3
+    if cfg.bound == "mfma":
+        roof["ffn_frac"] = (bf["gate_up"]["flops"] + bf["down"]["flops"]) / ffn_s / 1e12 / MFMA_F16_PEAK_TFLOPS
+    else:
+        roof["ffn_frac"] = (bf["gate_up"]["bytes"] + bf["down"]["bytes"]) / ffn_s / 1e9 / HBM_PEAK_GBS
+
+    rec = {
+        "metric": METRIC,
+        "value": cfg.T * args.steps / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.describe()}, NVFP4 W4A4 (E2M1 x E4M3/16 + fp32 global), "
+                               f"routed_scaling_factor {cfg.rsf}, REAP saliency every step",
+                   "operands": "nvfp4 codes decoded in registers to f16 for MFMA, f32 accumulate; routing in f64",
+                   "tokens_per_step": cfg.T, "experts": cfg.E, "top_k": cfg.k, "hidden": cfg.H,
+                   "intermediate": cfg.I, "touched_experts": bf["touched"]},
+        "stage_ms": ms_stage,
+        "roofline": roof,
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+/*
+ * moe_nvfp4.h -- C ABI of libmoe_nvfp4.so: the routed-expert MoE layer with
+ * NVFP4 W4A4 experts, on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (what the pages state):
+ *   - "K-EXAONE-152B-A23B-REAP-80E-NVFP4" model card, "Quantization Setup":
+ *     NVFP4 W4A4 -- FP4 E2M1 values, one FP8 E4M3 block scale per 16
+ *     elements, activations quantized dynamically against calibrated global
+ *     scales, round-to-nearest, per-expert Linear modules; the router
+ *     (mlp.gate) stays BF16.
+ *   - NetsPresso AQ blog, "The Standard NVFP4 Serving Spec": the double-scale
+ *     structure (an FP32 global scale times the E4M3 block scale).
+ *   - "K-EXAONE-152B-A23B-REAP-80E-BF16" model card, "Pruning Setup":
+ *     renormalized sigmoid routing with e_score_correction_bias,
+ *     routed_scaling_factor, and the REAP saliency
+ *     mean(topk_weight * ||f_e(x)||_2) over routed tokens.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Pointers   Every array pointer is a DEVICE pointer, allocated and owned by
+ *             the caller.  The library allocates and frees no device memory,
+ *             keeps no pointer after returning, and the caller keeps every
+ *             buffer alive until the enqueued work completes.
+ *  Streams    `stream` is a hipStream_t (NULL = the default stream).  Every
+ *             call only enqueues work and returns without synchronizing.
+ *  Sizes      int64_t element counts.  T = tokens, H = hidden size,
+ *             I = expert intermediate size, E = routed experts, k = top-k.
+ *             A pair is one (token t, slot j); its id is p = t*k + j.
+ *  NVFP4      A matrix [rows, cols] is stored as codes [rows, cols/2] (two
+ *             E2M1 codes per byte, element 2j in bits 3:0, element 2j+1 in
+ *             bits 7:4, bit 3 of a code = sign) plus scales [rows, cols/16]
+ *             (one E4M3-FN byte per 16 consecutive elements of a row) plus an
+ *             FP32 global scale gs.  value = e2m1(code) * e4m3(scale) / gs.
+ *             Quantization: s = f32(f32(amax16 / 6) * gs); S = E4M3 RNE,
+ *             saturating at 448; a zero S gives 16 zero codes; otherwise
+ *             code = E2M1 RNE-even(f32(x * f32(gs / S))), saturating at 6,
+ *             sign bit = sign bit of that product.
+ *  Weights    w13 codes [E, 2I, H/2], scales [E, 2I, H/16], gs [E, 2]:
+ *             rows 0..I-1 of an expert are the gate projection, rows I..2I-1
+ *             the up projection, each with its own global scale.
+ *             w2 codes [E, H, I/2], scales [E, H, I/16], gs [E].
+ *  Errors     Arguments are validated on the host before anything is
+ *             enqueued.  A failed check returns its status, enqueues nothing
+ *             and writes no output.  T == 0 (rows == 0) is a successful no-op
+ *             (moe_route still writes zero counts and offsets, reap_saliency
+ *             zero saliencies); pointers to zero-size arrays may be NULL.
+ *             A failed launch returns MOE_ERR_LAUNCH.  Faults inside a kernel
+ *             surface at the caller's next synchronization.  The message of
+ *             the last non-OK status of the calling thread is available from
+ *             moe_last_error().  No C++ exception crosses this interface.
+ *  Threads    Calls are stateless apart from the thread-local error message
+ *             and may be made from several host threads.
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_NVFP4_ABI_VERSION 1
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_NULL 1      /* a required pointer is NULL                                  */
+#define MOE_ERR_SHAPE 2     /* a size is out of range or inconsistent                      */
+#define MOE_ERR_ALIGN 3     /* a pointer or leading dimension is not aligned as required    */
+#define MOE_ERR_WORKSPACE 4 /* the workspace is NULL or smaller than the size query says    */
+#define MOE_ERR_DEVICE 5    /* no usable gfx950 device is current, or a HIP query failed    */
+#define MOE_ERR_LAUNCH 6    /* a kernel launch failed                                       */
+
+/* Message describing the last non-OK status returned on this host thread. */
+const char* moe_last_error(void);
+/* MOE_NVFP4_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Routing: sigmoid + bias top-k, renormalized and scaled, and the stable
+ * expert permutation ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card,
+ * "Pruning Setup"; "K-EXAONE-152B-A23B-REAP-80E-NVFP4" model card,
+ * "Quantization Setup": the router is BF16).
+ *
+ *   logit[t,e] = sum_h x[t,h] * w_router[e,h]   (BF16 products, FP64 sums)
+ *   s = sigmoid(logit) (FP64); score = s + bias[e]
+ *   topk_ids[t, 0..k-1]: the k largest scores, descending; equal scores go to
+ *     the lower expert index
+ *   topk_w[t,j] = rsf * s_j / sum_{selected} s   (FP64, stored FP32; the
+ *     bias selects, it does not enter the weights)
+ *   expert_counts[e] = number of pairs routed to e
+ *   expert_offsets[0..E] = exclusive prefix sum of the counts
+ *   sorted_pair_ids[offsets[e] .. offsets[e+1]) = the pair ids p routed to e,
+ *     in increasing order (a stable sort by expert)
+ *
+ * x_bf16 [T, ldx] (row-major, ldx >= H); w_router_bf16 [E, H]; bias [E]
+ * FP32; 1 <= k <= E <= 256; T * k < 2^31; routed_scaling_factor > 0.
+ * workspace: at least moe_route_workspace_bytes(T, E, k) bytes, 256-byte
+ * aligned, device memory; its contents on entry do not matter. */
+size_t moe_route_workspace_bytes(int64_t T, int64_t E, int64_t k);
+moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
+                     const uint16_t* w_router_bf16, const float* bias, int64_t E, int64_t k,
+                     float routed_scaling_factor, int32_t* topk_ids, float* topk_w,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic NVFP4 quantization of BF16 activations against a calibrated,
+ * static global scale ("K-EXAONE-152B-A23B-REAP-80E-NVFP4" model card,
+ * "Quantization Setup"; the double scale of the NetsPresso AQ blog,
+ * "The Standard NVFP4 Serving Spec").
+ *
+ * x_bf16 [rows, ld] with ld >= cols, ld % 8 == 0, 16-byte aligned;
+ * cols % 16 == 0; global_scale: device pointer to one FP32 (gs > 0).
+ * codes [rows, cols/2] and scales [rows, cols/16] are written densely
+ * (codes 8-byte aligned).  Bit-exact with the rule in the header comment. */
+moe_status nvfp4_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                              const float* global_scale, uint8_t* codes, uint8_t* scales_e4m3,
+                              void* stream);
+
+/* Offline round-to-nearest quantization of `batch` BF16 weight matrices
+ * [batch, rows, cols] (contiguous), each with its own global scale
+ * gs[b] = f32(2688 / amax(|W_b|)) (1 when W_b is all zero), written to
+ * global_scales [batch].  codes [batch, rows, cols/2], scales
+ * [batch, rows, cols/16].  For w13 pass batch = 2E, rows = I (gate and up
+ * are separate Linear modules, "per-expert Linear granularity"); for w2 pass
+ * batch = E, rows = H.  cols % 16 == 0; w_bf16 16-byte aligned. */
+moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t rows, int64_t cols,
+                                  uint8_t* codes, uint8_t* scales_e4m3, float* global_scales,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The grouped NVFP4 W4A4 expert FFN ("K-EXAONE-152B-A23B-REAP-80E-NVFP4"
+ * model card, "Quantization Setup": every routed expert Linear is W4A4):
+ *
+ *   for each expert e and each pair p in sorted_pair_ids[offsets[e]..):
+ *     t = p / k;  xhat = dequant(x_codes[t], x_scales[t], x_gs)
+ *     g = xhat . W_gate[e]^T, u = xhat . W_up[e]^T   (exact FP16 products of
+ *         the decoded values, FP32 accumulation)
+ *     h = silu(g) * u in FP32, quantized to NVFP4 with h_gs[e]
+ *     f = hhat . W_down[e]^T                          (same arithmetic)
+ *     pair_out[p, :] = topk_w[p] * f                  (FP32, [T*k, H])
+ *     pair_sqnorm[p] = sum_h f[h]^2 (unweighted f; only if pair_sqnorm != NULL)
+ *
+ * x_codes [T, H/2], x_scales [T, H/16] (from nvfp4_quantize_act), x_gs
+ * device FP32 [1]; weights in the layout of the header comment; h_gs [E]
+ * FP32 (calibrated); expert_offsets [E+1] and sorted_pair_ids [T*k] from
+ * moe_route; topk_w [T*k].  Requires H % 256 == 0, I % 128 == 0,
+ * 1 <= k <= E <= 256.  workspace: moe_ffn_workspace_bytes(...) bytes,
+ * 256-byte aligned; it holds the re-quantized h and the tile schedule.
+ * Pairs not listed in sorted_pair_ids are not written. */
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I);
+moe_status moe_nvfp4_grouped_ffn(
+    const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T, int64_t H,
+    const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+    const float* h_gs, int64_t E, int64_t I, int64_t k,
+    const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
+    float* pair_out, float* pair_sqnorm,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of moe_nvfp4_grouped_ffn as separate calls, with the
+ * re-quantized hidden state in caller memory: h_codes [T*k, I/2] and
+ * h_scales [T*k, I/16], row r = the r-th entry of sorted_pair_ids (grouped
+ * by expert).  Same requirements as above; their workspace is
+ * moe_ffn_stage_workspace_bytes(...) bytes. */
+size_t moe_ffn_stage_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I);
+moe_status moe_nvfp4_gate_up_swiglu(
+    const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T, int64_t H,
+    const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+    const float* h_gs, int64_t E, int64_t I, int64_t k,
+    const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+    uint8_t* h_codes, uint8_t* h_scales, void* workspace, size_t workspace_bytes, void* stream);
+moe_status moe_nvfp4_down_scatter(
+    const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs, int64_t T, int64_t H,
+    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int64_t E, int64_t I,
+    int64_t k, const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
+    float* pair_out, float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Weighted combine: y[t, :] = sum_{j=0..k-1} pair_out[t*k + j, :], summed in
+ * j order (deterministic).  pair_out already carries the routing weight
+ * ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card, "Pruning Setup":
+ * renormalized sigmoid routing weights).  out_dtype 0 writes BF16
+ * (round-to-nearest-even), 1 writes FP32.  H % 4 == 0; 16-byte aligned. */
+moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype,
+                       void* y, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* REAP saliency ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card, "Pruning
+ * Setup": mean(topk_weight * ||f_e(x)||_2) over routed tokens, with the
+ * model's sigmoid-and-bias routing weights including routed_scaling_factor):
+ *   saliency[e] = (sum over p routed to e of topk_w[p] * sqrt(pair_sqnorm[p]))
+ *                 / counts[e],   0 when no pair is routed to e.
+ * Summed in sorted_pair_ids order in FP64 (deterministic); written FP32. */
+moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w,
+                         const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                         int64_t T, int64_t k, int64_t E, float* saliency, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_NVFP4_H */

@@ -1,0 +1,338 @@
+// C ABI of libmoe_nvfp4.so (declared in include/moe_nvfp4.h).
+//
+// Every entry point validates its arguments on the host before making any HIP
+// call, so a rejected call enqueues nothing and touches no output.  Kernel
+// launches are asynchronous on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/moe_nvfp4.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// The current device must be gfx950; checked once per device id.
+moe_status check_device() {
+  static std::mutex mu;
+  static int ok_state[64] = {0};  // 0 unknown, 1 ok, -1 bad
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(MOE_ERR_DEVICE, "no current HIP device");
+  std::lock_guard<std::mutex> lk(mu);
+  if (ok_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed");
+    ok_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (ok_state[dev] < 0) {
+      char msg[300];
+      snprintf(msg, sizeof(msg), "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+      g_last_error = msg;
+    }
+  }
+  if (ok_state[dev] < 0) return MOE_ERR_DEVICE;
+  return MOE_OK;
+}
+
+moe_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ---- FFN workspace layout
+struct FfnWs {
+  size_t tile_expert, tile_row0, num_tiles, sq_part, h_codes, h_scales, total_stage, total_full;
+};
+
+FfnWs ffn_ws_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
+  FfnWs w{};
+  const int64_t tiles = moe::ffn_max_tiles(T, k, E);
+  size_t o = 0;
+  w.tile_expert = o;
+  o = round_up(o + (size_t)tiles * 4, 256);
+  w.tile_row0 = o;
+  o = round_up(o + (size_t)tiles * 4, 256);
+  w.num_tiles = o;
+  o = round_up(o + 4, 256);
+  w.sq_part = o;
+  o = round_up(o + (size_t)(T * k) * (size_t)moe::ffn_sq_parts(H) * 4, 256);
+  w.total_stage = o;
+  w.h_codes = o;
+  o = round_up(o + (size_t)(T * k) * (size_t)(I / 2), 256);
+  w.h_scales = o;
+  o = round_up(o + (size_t)(T * k) * (size_t)(I / 16), 256);
+  w.total_full = o;
+  return w;
+}
+
+moe_status check_ffn_shapes(int64_t T, int64_t H, int64_t E, int64_t I, int64_t k) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0 (got %lld)", (long long)T);
+  if (H <= 0 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "H must be a positive multiple of 256 (got %lld)", (long long)H);
+  if (I <= 0 || I % 128 != 0) return fail(MOE_ERR_SHAPE, "I must be a positive multiple of 128 (got %lld)", (long long)I);
+  if (k < 1 || E < k || E > 256) return fail(MOE_ERR_SHAPE, "need 1 <= k <= E <= 256 (k=%lld, E=%lld)", (long long)k, (long long)E);
+  if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t moe_abi_version(void) { return MOE_NVFP4_ABI_VERSION; }
+
+size_t moe_route_workspace_bytes(int64_t T, int64_t E, int64_t k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return moe::route_workspace_bytes(T, E, k);
+}
+
+moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx, const uint16_t* w_router_bf16,
+                     const float* bias, int64_t E, int64_t k, float routed_scaling_factor, int32_t* topk_ids,
+                     float* topk_w, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w_router_bf16 || !bias || !expert_counts || !expert_offsets ||
+      (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !sorted_pair_ids)))
+    return fail(MOE_ERR_NULL, "moe_route: a required pointer is NULL");
+  if (T < 0 || H < 1 || ldx < H) return fail(MOE_ERR_SHAPE, "moe_route: need T >= 0, H >= 1, ldx >= H");
+  if (k < 1 || E < k || E > 256) return fail(MOE_ERR_SHAPE, "moe_route: need 1 <= k <= E <= 256");
+  if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "moe_route: T*k must be < 2^31");
+  if (!(routed_scaling_factor > 0.0f)) return fail(MOE_ERR_SHAPE, "moe_route: routed_scaling_factor must be > 0");
+  const size_t need = moe::route_workspace_bytes(T, E, k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace needs %zu bytes", need);
+  if (need > 0 && !aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "moe_route: workspace must be 256-byte aligned");
+  if (moe_status s = check_device()) return s;
+  // T == 0 still writes zero counts and offsets.
+  return launched(moe::launch_route(x_bf16, T, H, ldx, w_router_bf16, bias, E, k, routed_scaling_factor, topk_ids,
+                                    topk_w, expert_counts, expert_offsets, sorted_pair_ids, workspace,
+                                    (hipStream_t)stream),
+                  "moe_route");
+}
+
+moe_status nvfp4_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                              const float* global_scale, uint8_t* codes, uint8_t* scales_e4m3, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || ld < cols)
+    return fail(MOE_ERR_SHAPE, "nvfp4_quantize_act: need rows >= 0, cols a positive multiple of 16, ld >= cols");
+  if (rows == 0) return MOE_OK;
+  if (!x_bf16 || !global_scale || !codes || !scales_e4m3)
+    return fail(MOE_ERR_NULL, "nvfp4_quantize_act: a required pointer is NULL");
+  if (ld % 8 != 0 || !aligned(x_bf16, 16) || !aligned(codes, 8))
+    return fail(MOE_ERR_ALIGN, "nvfp4_quantize_act: x must be 16-byte aligned with ld %% 8 == 0; codes 8-byte aligned");
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_quantize_bf16(x_bf16, rows, cols, ld, global_scale, rows, codes, scales_e4m3,
+                                            (hipStream_t)stream),
+                  "nvfp4_quantize_act");
+}
+
+moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
+                                  uint8_t* scales_e4m3, float* global_scales, void* stream) {
+  if (batch < 0 || rows <= 0 || cols <= 0 || cols % 16 != 0)
+    return fail(MOE_ERR_SHAPE, "nvfp4_quantize_weights: need batch >= 0, rows > 0, cols a positive multiple of 16");
+  if (batch == 0) return MOE_OK;
+  if (!w_bf16 || !codes || !scales_e4m3 || !global_scales)
+    return fail(MOE_ERR_NULL, "nvfp4_quantize_weights: a required pointer is NULL");
+  if (!aligned(w_bf16, 16) || !aligned(codes, 8))
+    return fail(MOE_ERR_ALIGN, "nvfp4_quantize_weights: w must be 16-byte aligned, codes 8-byte aligned");
+  if (moe_status s = check_device()) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (moe_status s = launched(moe::launch_weight_global_scales(w_bf16, batch, rows * cols, global_scales, st),
+                              "nvfp4_quantize_weights (global scales)"))
+    return s;
+  return launched(moe::launch_quantize_bf16(w_bf16, batch * rows, cols, cols, global_scales, rows, codes, scales_e4m3,
+                                            st),
+                  "nvfp4_quantize_weights");
+}
+
+size_t moe_ffn_stage_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
+  if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  return ffn_ws_layout(T, k, E, H, I).total_stage;
+}
+
+size_t moe_ffn_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
+  if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  return ffn_ws_layout(T, k, E, H, I).total_full;
+}
+
+static moe_status gate_up_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
+                               int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                               const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
+                               const int32_t* sorted_pair_ids, uint8_t* h_codes, uint8_t* h_scales,
+                               unsigned char* ws, hipStream_t st) {
+  const FfnWs L = ffn_ws_layout(T, k, E, H, I);
+  moe::FfnArgs a{};
+  a.a_codes = x_codes;
+  a.a_scales = x_scales;
+  a.b_codes = w13_codes;
+  a.b_scales = w13_scales;
+  a.a_gs = x_gs;
+  a.b_gs = w13_gs;
+  a.h_gs = h_gs;
+  a.K = H;
+  a.I = I;
+  a.H = H;
+  a.k = (int)k;
+  a.offsets = expert_offsets;
+  a.sorted = sorted_pair_ids;
+  a.tile_expert = reinterpret_cast<const int32_t*>(ws + L.tile_expert);
+  a.tile_row0 = reinterpret_cast<const int32_t*>(ws + L.tile_row0);
+  a.num_tiles = reinterpret_cast<const int32_t*>(ws + L.num_tiles);
+  a.h_codes = h_codes;
+  a.h_scales = h_scales;
+  return launched(moe::launch_ffn_stage(0, a, T, E, /*build_schedule=*/true, st), "moe_nvfp4_gate_up_swiglu");
+}
+
+static moe_status down_impl(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs, int64_t T, int64_t H,
+                            const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int64_t E,
+                            int64_t I, int64_t k, const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                            const float* topk_w, float* pair_out, float* pair_sqnorm, unsigned char* ws,
+                            bool build_schedule, hipStream_t st) {
+  const FfnWs L = ffn_ws_layout(T, k, E, H, I);
+  moe::FfnArgs a{};
+  a.a_codes = h_codes;
+  a.a_scales = h_scales;
+  a.b_codes = w2_codes;
+  a.b_scales = w2_scales;
+  a.a_gs = h_gs;
+  a.b_gs = w2_gs;
+  a.K = I;
+  a.I = I;
+  a.H = H;
+  a.k = (int)k;
+  a.offsets = expert_offsets;
+  a.sorted = sorted_pair_ids;
+  a.topk_w = topk_w;
+  a.tile_expert = reinterpret_cast<const int32_t*>(ws + L.tile_expert);
+  a.tile_row0 = reinterpret_cast<const int32_t*>(ws + L.tile_row0);
+  a.num_tiles = reinterpret_cast<const int32_t*>(ws + L.num_tiles);
+  a.pair_out = pair_out;
+  a.sq_part = pair_sqnorm ? reinterpret_cast<float*>(ws + L.sq_part) : nullptr;
+  a.n_part = moe::ffn_use_small(T) ? (int)(H / 64) : (int)(H / moe::ffn_tiled_bn());
+  if (moe_status s = launched(moe::launch_ffn_stage(1, a, T, E, build_schedule, st), "moe_nvfp4_down_scatter"))
+    return s;
+  if (pair_sqnorm)
+    return launched(moe::launch_sq_reduce(a.sq_part, T * k, a.n_part, pair_sqnorm, st), "moe_nvfp4_down_scatter (sq)");
+  return MOE_OK;
+}
+
+moe_status moe_nvfp4_gate_up_swiglu(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
+                                    int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                    const float* w13_gs, const float* h_gs, int64_t E, int64_t I, int64_t k,
+                                    const int32_t* expert_offsets, const int32_t* sorted_pair_ids, uint8_t* h_codes,
+                                    uint8_t* h_scales, void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status s = check_ffn_shapes(T, H, E, I, k)) return s;
+  if (T == 0) return MOE_OK;  // zero-size arrays may be NULL
+  if (!x_codes || !x_scales || !x_gs || !w13_codes || !w13_scales || !w13_gs || !h_gs || !expert_offsets ||
+      !sorted_pair_ids || !h_codes || !h_scales)
+    return fail(MOE_ERR_NULL, "moe_nvfp4_gate_up_swiglu: a required pointer is NULL");
+  if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(h_codes, 16) || !aligned(x_scales, 4) ||
+      !aligned(w13_scales, 4))
+    return fail(MOE_ERR_ALIGN, "moe_nvfp4_gate_up_swiglu: code arrays must be 16-byte and scale arrays 4-byte aligned");
+  const size_t need = ffn_ws_layout(T, k, E, H, I).total_stage;
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_gate_up_swiglu: workspace needs %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (moe_status s = check_device()) return s;
+  return gate_up_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, h_gs, E, I, k, expert_offsets,
+                      sorted_pair_ids, h_codes, h_scales, static_cast<unsigned char*>(workspace), (hipStream_t)stream);
+}
+
+moe_status moe_nvfp4_down_scatter(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs, int64_t T,
+                                  int64_t H, const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                                  int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
+                                  const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
+                                  float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status s = check_ffn_shapes(T, H, E, I, k)) return s;
+  if (T == 0) return MOE_OK;  // zero-size arrays may be NULL
+  if (!h_codes || !h_scales || !h_gs || !w2_codes || !w2_scales || !w2_gs || !expert_offsets || !sorted_pair_ids ||
+      !topk_w || !pair_out)
+    return fail(MOE_ERR_NULL, "moe_nvfp4_down_scatter: a required pointer is NULL");
+  if (!aligned(h_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) || !aligned(h_scales, 4) ||
+      !aligned(w2_scales, 4))
+    return fail(MOE_ERR_ALIGN, "moe_nvfp4_down_scatter: code arrays and pair_out must be 16-byte aligned");
+  const size_t need = ffn_ws_layout(T, k, E, H, I).total_stage;
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_down_scatter: workspace needs %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (moe_status s = check_device()) return s;
+  return down_impl(h_codes, h_scales, h_gs, T, H, w2_codes, w2_scales, w2_gs, E, I, k, expert_offsets,
+                   sorted_pair_ids, topk_w, pair_out, pair_sqnorm, static_cast<unsigned char*>(workspace),
+                   /*build_schedule=*/true, (hipStream_t)stream);
+}
+
+moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
+                                 int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                                 const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                                 const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
+                                 const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
+                                 float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status s = check_ffn_shapes(T, H, E, I, k)) return s;
+  if (T == 0) return MOE_OK;  // zero-size arrays may be NULL
+  if (!x_codes || !x_scales || !x_gs || !w13_codes || !w13_scales || !w13_gs || !w2_codes || !w2_scales || !w2_gs ||
+      !h_gs || !expert_offsets || !sorted_pair_ids || !topk_w || !pair_out)
+    return fail(MOE_ERR_NULL, "moe_nvfp4_grouped_ffn: a required pointer is NULL");
+  if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) ||
+      !aligned(x_scales, 4) || !aligned(w13_scales, 4) || !aligned(w2_scales, 4))
+    return fail(MOE_ERR_ALIGN, "moe_nvfp4_grouped_ffn: code arrays and pair_out must be 16-byte aligned");
+  const FfnWs L = ffn_ws_layout(T, k, E, H, I);
+  if (!workspace || workspace_bytes < L.total_full)
+    return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_grouped_ffn: workspace needs %zu bytes", L.total_full);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (moe_status s = check_device()) return s;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* h_codes = ws + L.h_codes;
+  uint8_t* h_scales = ws + L.h_scales;
+  if (moe_status s = gate_up_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, h_gs, E, I, k,
+                                  expert_offsets, sorted_pair_ids, h_codes, h_scales, ws, st))
+    return s;
+  // stage 2 reuses the schedule stage 1 built in the same workspace
+  return down_impl(h_codes, h_scales, h_gs, T, H, w2_codes, w2_scales, w2_gs, E, I, k, expert_offsets,
+                   sorted_pair_ids, topk_w, pair_out, pair_sqnorm, ws, /*build_schedule=*/false, st);
+}
+
+moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y,
+                       void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))
+    return fail(MOE_ERR_SHAPE, "moe_combine: need T >= 0, k >= 1, H a positive multiple of 4, out_dtype 0 or 1");
+  if (T == 0) return MOE_OK;
+  if (!pair_out || !y) return fail(MOE_ERR_NULL, "moe_combine: a required pointer is NULL");
+  if (!aligned(pair_out, 16) || !aligned(y, 16)) return fail(MOE_ERR_ALIGN, "moe_combine: 16-byte alignment required");
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_combine(pair_out, T, k, H, out_dtype, y, (hipStream_t)stream), "moe_combine");
+}
+
+moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w, const int32_t* expert_offsets,
+                         const int32_t* sorted_pair_ids, int64_t T, int64_t k, int64_t E, float* saliency,
+                         void* stream) {
+  if (!expert_offsets || !saliency || (T > 0 && (!pair_sqnorm || !topk_w || !sorted_pair_ids)))
+    return fail(MOE_ERR_NULL, "reap_saliency: a required pointer is NULL");
+  if (T < 0 || k < 1 || E < 1 || E > 256 || T * k >= (int64_t)1 << 31)
+    return fail(MOE_ERR_SHAPE, "reap_saliency: need T >= 0, k >= 1, 1 <= E <= 256");
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_reap(pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids, E, saliency,
+                                   (hipStream_t)stream),
+                  "reap_saliency");
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device helpers shared by the gfx950 kernels: NVFP4 element encoders, the
+// exact FP4 x E4M3 -> FP16 decode that feeds the 16-bit MFMA, and small
+// wave-level utilities.
+//
+// Format facts used here ("K-EXAONE-152B-A23B-REAP-80E-NVFP4" model card,
+// "Quantization Setup": FP4 E2M1 values, group 16, FP8 E4M3 block scales):
+//   E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7, bit 3 = sign);
+//   E4M3-FN value 2^(e-7) * (1 + m/8), subnormal 2^-6 * m/8, max 448 (0x7E).
+// A decoded element code * S has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is exact in FP16 (normal range); the product of two
+// decoded elements is exact in FP32, and the MFMA accumulates in FP32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr float kE2M1Max = 6.0f;
+constexpr float kE4M3Max = 448.0f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// E4M3-FN round-to-nearest-even of a non-negative float, saturating at 448.
+// Normal range: round the float32 mantissa to 3 bits in integer arithmetic
+// (carry into the exponent is the correct rounding).  Below 2^-6 the E4M3
+// grid is uniform with step 2^-9, so the code is rint(s * 512) (ties to even),
+// and 8 there is the smallest normal code 0x08, which is also correct.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float s) {
+  if (!(s < kE4M3Max)) return 0x7Eu;  // >= 448, +inf
+  if (s < 0.015625f) return (uint32_t)__builtin_rintf(s * 512.0f);
+  uint32_t b = __float_as_uint(s);
+  uint32_t t = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;  // biased exp << 3 | mant3, rounded
+  uint32_t code = t - ((127u - 7u) << 3);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Value of an E4M3 byte with sign bit 0 (block scales are never negative).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 0) return (float)m * 0.001953125f;  // m * 2^-9, exact
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 round-to-nearest-even of a float, saturating at 6; sign from the sign
+// bit of v.  Each comparison is one decision boundary of the value set; at
+// the boundary itself the tie goes to the even code: 0.25 -> 0, 0.75 -> 1.0,
+// 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  float a = __builtin_fabsf(v);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Quantize one block of 16 floats against global scale gs.  Returns the E4M3
+// scale byte; writes 8 packed code bytes (element 2j in the low nibble) into
+// lo (bytes 0..3) and hi (bytes 4..7).  Every step is one IEEE float32
+// operation in the order s = (amax / 6) * gs, inv = gs / S, v = x * inv.
+__device__ __forceinline__ uint32_t quantize_block16(const float* x, float gs, uint32_t& lo, uint32_t& hi) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  float s = amax / kE2M1Max;
+  s = s * gs;
+  uint32_t sc = e4m3_encode_nonneg(s);
+  float sd = e4m3_to_f32(sc);
+  lo = 0;
+  hi = 0;
+  if (sd != 0.0f) {
+    float inv = gs / sd;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= e2m1_encode(x[i] * inv) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= e2m1_encode(x[8 + i] * inv) << (4 * i);
+  }
+  return sc;
+}
+
+// Decode 8 packed E2M1 codes (one dword, element 0 in bits 3:0) times the
+// block scale S (given as FP16, exact) into 8 FP16 values for an MFMA
+// operand.  The scaled convert applies only the exponent of its scale
+// operand, so it converts with scale 1 and an exact packed FP16 multiply
+// applies the full E4M3 value.
+__device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s2) {
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ half2_t scale_pair(uint32_t scale_byte) {
+  _Float16 h = (_Float16)e4m3_to_f32(scale_byte);
+  half2_t r;
+  r[0] = h;
+  r[1] = h;
+  return r;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+}  // namespace moe

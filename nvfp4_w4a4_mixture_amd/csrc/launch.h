@@ -1,0 +1,63 @@
+// Internal launcher interface between the C-ABI host code (api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Arguments of one FFN stage (gate_up: A = x, B = w13; down: A = h, B = w2).
+struct FfnArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  const float* a_gs;  // gate_up: x_gs [1]; down: h_gs [E]
+  const float* b_gs;  // gate_up: w13_gs [E, 2]; down: w2_gs [E]
+  const float* h_gs;  // gate_up: h_gs [E]
+  int64_t K;          // reduction length (H or I)
+  int64_t I;
+  int64_t H;
+  int k;
+  const int32_t* offsets;
+  const int32_t* sorted;
+  const float* topk_w;
+  const int32_t* tile_expert;  // tiled schedule (workspace)
+  const int32_t* tile_row0;
+  const int32_t* num_tiles;
+  uint8_t* h_codes;  // gate_up output
+  uint8_t* h_scales;
+  float* pair_out;  // down outputs
+  float* sq_part;   // [T*k, n_part] partial sums of f^2, or null
+  int n_part;
+};
+
+hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* gs,
+                                int64_t rows_per_gs, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_weight_global_scales(const uint16_t* w, int64_t batch, int64_t per_matrix, float* gs,
+                                       hipStream_t stream);
+
+size_t route_workspace_bytes(int64_t T, int64_t E, int64_t k);
+hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, const float* bias,
+                        int64_t E, int64_t k, float rsf, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted, void* workspace, hipStream_t st);
+
+int64_t ffn_max_tiles(int64_t T, int64_t k, int64_t E);
+int ffn_sq_parts(int64_t H);
+bool ffn_use_small(int64_t T);
+int ffn_tiled_bm();
+int ffn_tiled_hcols();
+int ffn_tiled_bn();
+// build_schedule: (re)build the tiled kernel's m-tile schedule in the workspace
+// from expert_offsets before launching; a second stage of the same call may reuse it.
+hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool build_schedule, hipStream_t st);
+hipError_t launch_sq_reduce(const float* part, int64_t npairs, int n_part, float* out, hipStream_t st);
+
+hipError_t launch_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
+                          hipStream_t st);
+hipError_t launch_reap(const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
+                       int64_t E, float* saliency, hipStream_t st);
+
+}  // namespace moe

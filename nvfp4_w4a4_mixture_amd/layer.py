@@ -1,0 +1,117 @@
+"""The routed NVFP4 W4A4 MoE layer as one object: the C-ABI calls in order.
+
+forward(x):  moe_route -> nvfp4_quantize_act -> moe_nvfp4_gate_up_swiglu ->
+             moe_nvfp4_down_scatter -> moe_combine (-> reap_saliency)
+(the two FFN calls are the stages of moe_nvfp4_grouped_ffn)
+All buffers for a given token count are allocated once and reused, so a
+forward pass enqueues only kernels on the current stream.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import ops
+
+
+@dataclass
+class LayerOut:
+    y: torch.Tensor
+    route: ops.RouteOut
+    x_codes: torch.Tensor
+    x_scales: torch.Tensor
+    pair_out: torch.Tensor
+    pair_sqnorm: Optional[torch.Tensor]
+    saliency: Optional[torch.Tensor]
+
+
+class NVFP4MoELayer:
+    def __init__(self, w_router_bf16, bias, k: int, rsf: float, x_gs, h_gs, w13_codes, w13_scales, w13_gs,
+                 w2_codes, w2_scales, w2_gs):
+        self.w_router = w_router_bf16
+        self.bias = bias
+        self.k = int(k)
+        self.rsf = float(rsf)
+        self.x_gs = x_gs.reshape(1)
+        self.h_gs = h_gs
+        self.w13 = (w13_codes, w13_scales, w13_gs)
+        self.w2 = (w2_codes, w2_scales, w2_gs)
+        self.E, two_i, h_half = w13_codes.shape
+        self.H, self.I = 2 * h_half, two_i // 2
+        self.device = w13_codes.device
+        self._bufs: dict = {}
+
+    @classmethod
+    def from_bf16(cls, w_router_bf16, bias, k, rsf, x_gs, h_gs, w13_bf16, w2_bf16):
+        """Quantize BF16 expert weights with the library (offline RTN, per expert Linear).
+
+        w13_bf16 [E, 2I, H] (gate rows then up rows), w2_bf16 [E, H, I]."""
+        E, two_i, H = w13_bf16.shape
+        I = two_i // 2
+        c13, s13, g13 = ops.nvfp4_quantize_weights(w13_bf16.view(2 * E, I, H))
+        c2, s2, g2 = ops.nvfp4_quantize_weights(w2_bf16)
+        return cls(w_router_bf16, bias, k, rsf, x_gs, h_gs, c13.view(E, 2 * I, H // 2), s13.view(E, 2 * I, H // 16),
+                   g13.view(E, 2), c2, s2, g2)
+
+    def _buffers(self, T: int, reap: bool, out_dtype: torch.dtype):
+        key = (T, reap, out_dtype)
+        b = self._bufs.get(key)
+        if b is None:
+            d, E, H, I, k = self.device, self.E, self.H, self.I, self.k
+            b = dict(
+                route=ops.RouteOut(torch.empty((T, k), dtype=torch.int32, device=d),
+                                   torch.empty((T, k), dtype=torch.float32, device=d),
+                                   torch.empty((E,), dtype=torch.int32, device=d),
+                                   torch.empty((E + 1,), dtype=torch.int32, device=d),
+                                   torch.empty((T * k,), dtype=torch.int32, device=d)),
+                route_ws=torch.empty((max(ops.moe_route_workspace_bytes(T, E, k), 1),), dtype=torch.uint8, device=d),
+                x_codes=torch.empty((T, H // 2), dtype=torch.uint8, device=d),
+                x_scales=torch.empty((T, H // 16), dtype=torch.uint8, device=d),
+                pair_out=torch.empty((T * k, H), dtype=torch.float32, device=d),
+                pair_sqnorm=torch.empty((T * k,), dtype=torch.float32, device=d) if reap else None,
+                h_codes=torch.empty((T * k, I // 2), dtype=torch.uint8, device=d),
+                h_scales=torch.empty((T * k, I // 16), dtype=torch.uint8, device=d),
+                ffn_ws=torch.empty((max(ops.moe_ffn_stage_workspace_bytes(T, k, E, H, I), 1),), dtype=torch.uint8,
+                                   device=d),
+                y=torch.empty((T, H), dtype=out_dtype, device=d),
+                saliency=torch.empty((E,), dtype=torch.float32, device=d) if reap else None,
+            )
+            self._bufs[key] = b
+        return b
+
+    STAGES = ("route", "quantize", "gate_up", "down", "combine", "reap")
+
+    def forward(self, x_bf16: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, reap: bool = False,
+                events: Optional[list] = None) -> LayerOut:
+        """One layer pass.  If `events` is a list of len(STAGES) + 1 timing events,
+        they are recorded on the current stream around each stage."""
+        T = x_bf16.shape[0]
+        b = self._buffers(T, reap, out_dtype)
+        mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        mark(0)
+        r = ops.moe_route(x_bf16, self.w_router, self.bias, self.k, self.rsf, out=b["route"], workspace=b["route_ws"])
+        mark(1)
+        ops.nvfp4_quantize_act(x_bf16, self.x_gs, b["x_codes"], b["x_scales"])
+        mark(2)
+        # the two stages of moe_nvfp4_grouped_ffn, called separately so each can be timed
+        ops.moe_nvfp4_gate_up_swiglu(b["x_codes"], b["x_scales"], self.x_gs, *self.w13, self.h_gs, self.k,
+                                     r.expert_offsets, r.sorted_pair_ids, b["h_codes"], b["h_scales"],
+                                     workspace=b["ffn_ws"])
+        mark(3)
+        ops.moe_nvfp4_down_scatter(b["h_codes"], b["h_scales"], self.h_gs, T, *self.w2, self.k, r.expert_offsets,
+                                   r.sorted_pair_ids, r.topk_w, pair_out=b["pair_out"],
+                                   pair_sqnorm=b["pair_sqnorm"] if reap else None, workspace=b["ffn_ws"])
+        mark(4)
+        ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
+        mark(5)
+        sal = None
+        if reap:
+            sal = ops.reap_saliency(b["pair_sqnorm"], r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, self.k,
+                                    self.E, out=b["saliency"])
+        mark(6)
+        return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal)
+
+    __call__ = forward

@@ -1,0 +1,232 @@
+"""Python binding of the C ABI, one function per entry point, same names.
+
+Argument marshalling only: each function checks tensor shapes/dtypes/devices,
+allocates missing outputs with torch (device memory), passes raw pointers and
+the current HIP stream to the library, and raises :class:`MoEError` on a
+non-OK status.  Every step of the layer runs in the library's HIP kernels.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import NamedTuple, Optional
+
+import torch
+
+from ._lib import MoEError, check, lib  # noqa: F401
+
+__all__ = ["moe_route", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
+           "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
+           "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, contiguous: bool = True) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        return ws
+    # torch's caching allocator returns 256-byte aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def moe_route_workspace_bytes(T: int, E: int, k: int) -> int:
+    return int(lib().moe_route_workspace_bytes(T, E, k))
+
+
+def moe_ffn_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_ffn_workspace_bytes(T, k, E, H, I))
+
+
+def moe_ffn_stage_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
+    return int(lib().moe_ffn_stage_workspace_bytes(T, k, E, H, I))
+
+
+class RouteOut(NamedTuple):
+    topk_ids: torch.Tensor  # [T, k] int32
+    topk_w: torch.Tensor  # [T, k] float32
+    expert_counts: torch.Tensor  # [E] int32
+    expert_offsets: torch.Tensor  # [E+1] int32
+    sorted_pair_ids: torch.Tensor  # [T*k] int32
+
+
+def moe_route(x_bf16: torch.Tensor, w_router_bf16: torch.Tensor, bias: torch.Tensor, k: int,
+              routed_scaling_factor: float, out: Optional[RouteOut] = None,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> RouteOut:
+    if x_bf16.dim() != 2 or (x_bf16.numel() > 0 and x_bf16.stride(1) != 1):
+        raise ValueError("x_bf16 must be [T, H] with unit column stride")
+    _need(x_bf16, "x_bf16", torch.bfloat16, contiguous=False)
+    T, H = x_bf16.shape
+    ldx = x_bf16.stride(0) if T > 0 else H
+    E = w_router_bf16.shape[0]
+    _need(w_router_bf16, "w_router_bf16", torch.bfloat16, (E, H))
+    _need(bias, "bias", torch.float32, (E,))
+    dev = x_bf16.device
+    if out is None:
+        out = RouteOut(torch.empty((T, k), dtype=torch.int32, device=dev),
+                       torch.empty((T, k), dtype=torch.float32, device=dev),
+                       torch.empty((E,), dtype=torch.int32, device=dev),
+                       torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                       torch.empty((T * k,), dtype=torch.int32, device=dev))
+    nbytes = moe_route_workspace_bytes(T, E, k)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().moe_route(_p(x_bf16), T, H, ldx, _p(w_router_bf16), _p(bias), E, k,
+                         float(routed_scaling_factor), _p(out.topk_ids), _p(out.topk_w), _p(out.expert_counts),
+                         _p(out.expert_offsets), _p(out.sorted_pair_ids), _p(ws), ws.numel(), _stream(stream))
+    check(st, "moe_route")
+    return out
+
+
+def nvfp4_quantize_act(x_bf16: torch.Tensor, global_scale: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None, stream=None):
+    if x_bf16.dim() != 2 or (x_bf16.numel() > 0 and x_bf16.stride(1) != 1):
+        raise ValueError("x_bf16 must be [rows, cols] with unit column stride")
+    _need(x_bf16, "x_bf16", torch.bfloat16, contiguous=False)
+    _need(global_scale, "global_scale", torch.float32, (1,))
+    rows, cols = x_bf16.shape
+    ld = x_bf16.stride(0) if rows > 0 else cols
+    dev = x_bf16.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    st = lib().nvfp4_quantize_act(_p(x_bf16), rows, cols, ld, _p(global_scale), _p(codes),
+                                  _p(scales), _stream(stream))
+    check(st, "nvfp4_quantize_act")
+    return codes, scales
+
+
+def nvfp4_quantize_weights(w_bf16: torch.Tensor, stream=None):
+    """w_bf16 [batch, rows, cols] -> (codes [batch, rows, cols/2], scales [batch, rows, cols/16], gs [batch])."""
+    _need(w_bf16, "w_bf16", torch.bfloat16)
+    if w_bf16.dim() != 3:
+        raise ValueError("w_bf16 must be [batch, rows, cols]")
+    b, r, c = w_bf16.shape
+    dev = w_bf16.device
+    codes = torch.empty((b, r, c // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((b, r, c // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty((b,), dtype=torch.float32, device=dev)
+    st = lib().nvfp4_quantize_weights(_p(w_bf16), b, r, c, _p(codes), _p(scales), _p(gs), _stream(stream))
+    check(st, "nvfp4_quantize_weights")
+    return codes, scales, gs
+
+
+def _ffn_dims(x_codes, w13_codes, w2_codes):
+    T = x_codes.shape[0]
+    E, two_i, h_half = w13_codes.shape
+    return T, 2 * h_half, E, two_i // 2
+
+
+def moe_nvfp4_grouped_ffn(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs,
+                          h_gs, k: int, expert_offsets, sorted_pair_ids, topk_w, pair_out=None,
+                          pair_sqnorm: Optional[torch.Tensor] | bool = None, workspace=None, stream=None):
+    T, H, E, I = _ffn_dims(x_codes, w13_codes, w2_codes)
+    _need(x_codes, "x_codes", torch.uint8, (T, H // 2))
+    _need(x_scales, "x_scales", torch.uint8, (T, H // 16))
+    _need(x_gs, "x_gs", torch.float32, (1,))
+    _need(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, H // 2))
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 16))
+    _need(w13_gs, "w13_gs", torch.float32, (E, 2))
+    _need(w2_codes, "w2_codes", torch.uint8, (E, H, I // 2))
+    _need(w2_scales, "w2_scales", torch.uint8, (E, H, I // 16))
+    _need(w2_gs, "w2_gs", torch.float32, (E,))
+    _need(h_gs, "h_gs", torch.float32, (E,))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _need(sorted_pair_ids, "sorted_pair_ids", torch.int32, (T * k,))
+    _need(topk_w, "topk_w", torch.float32)
+    dev = x_codes.device
+    if pair_out is None:
+        pair_out = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    if pair_sqnorm is True:
+        pair_sqnorm = torch.empty((T * k,), dtype=torch.float32, device=dev)
+    elif pair_sqnorm is False:
+        pair_sqnorm = None
+    ws = _workspace(moe_ffn_workspace_bytes(T, k, E, H, I), dev, workspace)
+    st = lib().moe_nvfp4_grouped_ffn(_p(x_codes), _p(x_scales), _p(x_gs), T, H, _p(w13_codes), _p(w13_scales),
+                                     _p(w13_gs), _p(w2_codes), _p(w2_scales), _p(w2_gs), _p(h_gs), E, I, k,
+                                     _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w), _p(pair_out),
+                                     _p(pair_sqnorm), _p(ws), ws.numel(), _stream(stream))
+    check(st, "moe_nvfp4_grouped_ffn")
+    return pair_out, pair_sqnorm
+
+
+def moe_nvfp4_gate_up_swiglu(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs, h_gs, k: int,
+                             expert_offsets, sorted_pair_ids, h_codes=None, h_scales=None, workspace=None,
+                             stream=None):
+    T = x_codes.shape[0]
+    E, two_i, h_half = w13_codes.shape
+    H, I = 2 * h_half, two_i // 2
+    _need(x_codes, "x_codes", torch.uint8, (T, H // 2))
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 16))
+    dev = x_codes.device
+    if h_codes is None:
+        h_codes = torch.empty((T * k, I // 2), dtype=torch.uint8, device=dev)
+    if h_scales is None:
+        h_scales = torch.empty((T * k, I // 16), dtype=torch.uint8, device=dev)
+    ws = _workspace(moe_ffn_stage_workspace_bytes(T, k, E, H, I), dev, workspace)
+    st = lib().moe_nvfp4_gate_up_swiglu(_p(x_codes), _p(x_scales), _p(x_gs), T, H, _p(w13_codes), _p(w13_scales),
+                                        _p(w13_gs), _p(h_gs), E, I, k, _p(expert_offsets), _p(sorted_pair_ids),
+                                        _p(h_codes), _p(h_scales), _p(ws), ws.numel(), _stream(stream))
+    check(st, "moe_nvfp4_gate_up_swiglu")
+    return h_codes, h_scales
+
+
+def moe_nvfp4_down_scatter(h_codes, h_scales, h_gs, T: int, w2_codes, w2_scales, w2_gs, k: int, expert_offsets,
+                           sorted_pair_ids, topk_w, pair_out=None, pair_sqnorm=None, workspace=None, stream=None):
+    E, H, i_half = w2_codes.shape
+    I = 2 * i_half
+    _need(h_codes, "h_codes", torch.uint8, (T * k, I // 2))
+    dev = h_codes.device
+    if pair_out is None:
+        pair_out = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    if pair_sqnorm is True:
+        pair_sqnorm = torch.empty((T * k,), dtype=torch.float32, device=dev)
+    elif pair_sqnorm is False:
+        pair_sqnorm = None
+    ws = _workspace(moe_ffn_stage_workspace_bytes(T, k, E, H, I), dev, workspace)
+    st = lib().moe_nvfp4_down_scatter(_p(h_codes), _p(h_scales), _p(h_gs), T, H, _p(w2_codes), _p(w2_scales),
+                                      _p(w2_gs), E, I, k, _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w),
+                                      _p(pair_out), _p(pair_sqnorm), _p(ws), ws.numel(), _stream(stream))
+    check(st, "moe_nvfp4_down_scatter")
+    return pair_out, pair_sqnorm
+
+
+def moe_combine(pair_out: torch.Tensor, T: int, k: int, out_dtype: torch.dtype = torch.bfloat16, y=None,
+                stream=None) -> torch.Tensor:
+    _need(pair_out, "pair_out", torch.float32)
+    H = pair_out.shape[1]
+    code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
+    if y is None:
+        y = torch.empty((T, H), dtype=out_dtype, device=pair_out.device)
+    st = lib().moe_combine(_p(pair_out), T, k, H, code, _p(y), _stream(stream))
+    check(st, "moe_combine")
+    return y
+
+
+def reap_saliency(pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids, T: int, k: int, E: int, out=None,
+                  stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((E,), dtype=torch.float32, device=pair_sqnorm.device)
+    st = lib().reap_saliency(_p(pair_sqnorm), _p(topk_w), _p(expert_offsets), _p(sorted_pair_ids), T, k, E,
+                             _p(out), _stream(stream))
+    check(st, "reap_saliency")
+    return out

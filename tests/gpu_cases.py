@@ -1,0 +1,140 @@
+"""Shared helpers for the GPU parity tests: seeded cases on both sides and comparisons.
+
+The oracle quantizes its own copy of every weight; the GPU path quantizes with
+the library.  Inputs come from seeded numpy draws (or workloads.gen); the
+calibrated global scales of a random case come from the oracle's calibration
+(an input to both sides).  Nothing flows from the GPU path into the oracle.
+"""
+
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from oracle import moe as omoe
+from oracle import nvfp4 as onv
+from oracle import routing as oroute
+from workloads import gen
+
+NEAR_TIE = 1e-9
+
+
+def say(msg: str) -> None:
+    """Name the case on stdout before a GPU step, so a fault can be attributed."""
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    return gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(np.asarray(a, np.float32))).astype(np.float64)
+
+
+@dataclass
+class Case:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    rsf: float
+    x: np.ndarray  # [T, H] bf16 bits
+    wr: np.ndarray  # [E, H] bf16 bits
+    bias: np.ndarray  # [E] f32
+    gate: list  # per expert [I, H] bf16 bits
+    up: list
+    down: list  # per expert [H, I] bf16 bits
+    gs_x: np.float32
+    gs_h: np.ndarray  # [E] f32
+    experts_q: list  # oracle ExpertQ per expert
+
+    def w13_bf16(self, device="cuda") -> torch.Tensor:
+        w = np.stack([np.concatenate([g, u], axis=0) for g, u in zip(self.gate, self.up)])
+        return dev_bf16(w, device)
+
+    def w2_bf16(self, device="cuda") -> torch.Tensor:
+        return dev_bf16(np.stack(self.down), device)
+
+
+def random_case(name, seed, T, H, I, E, k, rsf=2.5, wscale=0.02, xscale=1.0, bias_range=0.1, n_cal=64) -> Case:
+    rng = np.random.default_rng(seed)
+    bf = lambda a: gen.f32_to_bf16_bits(np.asarray(a, np.float32))  # noqa: E731
+    x = bf(rng.standard_normal((T, H)) * xscale)
+    wr = bf(rng.standard_normal((E, H)) * 0.02)
+    bias = rng.uniform(-bias_range, bias_range, E).astype(np.float32)
+    gate = [bf(rng.standard_normal((I, H)) * wscale) for _ in range(E)]
+    up = [bf(rng.standard_normal((I, H)) * wscale) for _ in range(E)]
+    down = [bf(rng.standard_normal((H, I)) * wscale) for _ in range(E)]
+    f32 = gen.bf16_bits_to_f32
+    experts_q = [omoe.quantize_expert(f32(g), f32(u), f32(d)) for g, u, d in zip(gate, up, down)]
+    x_cal = bf(rng.standard_normal((n_cal, H)) * xscale)
+    gs_x, gs_h = omoe.calibrate(x_cal, experts_q, E)
+    return Case(name, T, H, I, E, k, rsf, x, wr, bias, gate, up, down, gs_x, gs_h, experts_q)
+
+
+def config_case(cfg, T=None, experts=None) -> Case:
+    """A workload config's inputs (optionally fewer tokens) with oracle-quantized experts (lazily: only `experts`)."""
+    ws = cfg.weights
+    x = gen.tokens(cfg, T)
+    gs_x, gs_h = gen.global_scales(ws)
+    gate, up, down, q = [None] * ws.E, [None] * ws.E, [None] * ws.E, [None] * ws.E
+    for e, g, u, d in gen.iter_experts_bf16(ws, experts):
+        gate[e], up[e], down[e] = g, u, d
+        f32 = gen.bf16_bits_to_f32
+        q[e] = omoe.quantize_expert(f32(g), f32(u), f32(d))
+    return Case(cfg.name, x.shape[0], ws.H, ws.I, ws.E, cfg.k, cfg.rsf, x, gen.router_weight(ws),
+                gen.router_bias(cfg), gate, up, down, gs_x, gs_h, q)
+
+
+def gpu_layer(case: Case, device="cuda"):
+    from nvfp4_w4a4_mixture_amd.layer import NVFP4MoELayer
+
+    return NVFP4MoELayer.from_bf16(dev_bf16(case.wr, device), torch.from_numpy(case.bias).to(device), case.k,
+                                   case.rsf, torch.tensor([case.gs_x], dtype=torch.float32, device=device),
+                                   torch.from_numpy(case.gs_h).to(device), case.w13_bf16(device),
+                                   case.w2_bf16(device))
+
+
+def oracle_layer(case: Case, tokens=None, with_pairs=False) -> dict:
+    return omoe.moe_layer(case.x, case.wr, case.bias, case.k, case.rsf, case.gs_x, case.experts_q, case.gs_h,
+                          tokens=tokens, with_pairs=with_pairs)
+
+
+def check_routing(ids_gpu, w_gpu, ref: dict, rsf: float, E: int) -> int:
+    """Bitwise ids where the oracle's top-k margin is >= NEAR_TIE; returns the number of near-tie tokens.
+
+    For near-tie tokens the GPU choice must still be a valid top-k (its k-th
+    score within NEAR_TIE of the oracle's)."""
+    ids_ref, gap = ref["ids"], ref["gap"]
+    clear = gap >= NEAR_TIE
+    assert np.array_equal(ids_gpu[clear], ids_ref[clear]), "top-k ids differ"
+    assert np.all(np.abs(w_gpu[clear].astype(np.float64) - ref["weights64"][clear]) <= 1e-6 * rsf), "topk_w differ"
+    return int((~clear).sum())
+
+
+def oracle_codes(case: Case):
+    """Oracle quantization of x: (packed codes [T, H/2], scales [T, H/16])."""
+    c, s = onv.quantize(gen.bf16_bits_to_f32(case.x), case.gs_x)
+    return onv.pack_codes(c), s
+
+
+def oracle_perm(ids: np.ndarray, E: int):
+    return oroute.permute(ids, E)

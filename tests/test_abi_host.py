@@ -1,0 +1,150 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/moe_nvfp4.h declares;
+* every validation failure returns its documented status before any HIP call
+  (fake, aligned, non-null addresses are never dereferenced on this path);
+* workspace size queries are consistent.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_nvfp4.h")
+
+OK, NULL, SHAPE, ALIGN, WORKSPACE = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(0x10000)  # aligned fake device address; validation fails before any use
+P2 = ctypes.c_void_p(0x20000)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from nvfp4_w4a4_mixture_amd import _lib
+
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"sizeof"})
+
+
+def test_header_symbols_exported(L):
+    names = header_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_signatures_cover_header():
+    from nvfp4_w4a4_mixture_amd import _lib
+
+    assert sorted(_lib.SIGNATURES) == header_functions()
+
+
+def test_version(L):
+    assert L.moe_abi_version() == 1
+
+
+def _route(L, x=P, T=4, H=64, ldx=64, wr=P, bias=P, E=8, k=2, rsf=2.5, ws=P2, wsb=1 << 20):
+    return L.moe_route(x, T, H, ldx, wr, bias, E, k, rsf, P, P, P, P, P, ws, wsb, None)
+
+
+def test_route_validation(L):
+    assert _route(L, x=None) == NULL
+    assert _route(L, bias=None) == NULL
+    assert _route(L, T=-1) == SHAPE
+    assert _route(L, ldx=32) == SHAPE
+    assert _route(L, k=0) == SHAPE
+    assert _route(L, k=9, E=8) == SHAPE
+    assert _route(L, E=257, k=8) == SHAPE
+    assert _route(L, rsf=0.0) == SHAPE
+    assert _route(L, ws=None) == WORKSPACE
+    assert _route(L, wsb=4) == WORKSPACE
+    assert _route(L, ws=ctypes.c_void_p(0x10008)) == ALIGN
+    assert b"moe_route" in L.moe_last_error()
+
+
+def test_quantize_act_validation(L):
+    q = L.nvfp4_quantize_act
+    assert q(None, 4, 64, 64, P, P, P, None) == NULL
+    assert q(P, 4, 60, 64, P, P, P, None) == SHAPE  # cols % 16
+    assert q(P, 4, 64, 32, P, P, P, None) == SHAPE  # ld < cols
+    assert q(P, -1, 64, 64, P, P, P, None) == SHAPE
+    assert q(P, 4, 64, 68, P, P, P, None) == ALIGN  # ld % 8
+    assert q(ctypes.c_void_p(0x10002), 4, 64, 64, P, P, P, None) == ALIGN
+    assert q(P, 4, 64, 64, P, ctypes.c_void_p(0x10004), P, None) == ALIGN
+    assert q(P, 0, 64, 64, P, P, P, None) == OK  # no rows: no-op, no device call
+
+
+def test_quantize_weights_validation(L):
+    q = L.nvfp4_quantize_weights
+    assert q(P, 2, 16, 64, P, P, None, None) == NULL
+    assert q(P, 2, 16, 40, P, P, P, None) == SHAPE
+    assert q(P, 2, 0, 64, P, P, P, None) == SHAPE
+    assert q(ctypes.c_void_p(0x10008), 2, 16, 64, P, P, P, None) == ALIGN
+    assert q(P, 0, 16, 64, P, P, P, None) == OK
+
+
+def _ffn(L, T=16, H=256, E=8, I=128, k=2, ws=P2, wsb=1 << 30, xc=P, sq=None, po=P):
+    return L.moe_nvfp4_grouped_ffn(xc, P, P, T, H, P, P, P, P, P, P, P, E, I, k, P, P, P, po, sq, ws, wsb, None)
+
+
+def test_ffn_validation(L):
+    assert _ffn(L, xc=None) == NULL
+    assert _ffn(L, po=None) == NULL
+    assert _ffn(L, H=200) == SHAPE  # H % 256
+    assert _ffn(L, I=96) == SHAPE  # I % 128
+    assert _ffn(L, k=9, E=8) == SHAPE
+    assert _ffn(L, E=300, k=8) == SHAPE
+    assert _ffn(L, T=-2) == SHAPE
+    assert _ffn(L, ws=None) == WORKSPACE
+    assert _ffn(L, wsb=16) == WORKSPACE
+    assert _ffn(L, xc=ctypes.c_void_p(0x10008)) == ALIGN
+    assert _ffn(L, po=ctypes.c_void_p(0x10004)) == ALIGN
+    assert _ffn(L, ws=ctypes.c_void_p(0x10010)) == ALIGN
+    assert _ffn(L, T=0) == OK  # no pairs: no-op
+
+
+def test_ffn_workspace_queries(L):
+    full = L.moe_ffn_workspace_bytes(8192, 8, 80, 6144, 2048)
+    stage = L.moe_ffn_stage_workspace_bytes(8192, 8, 80, 6144, 2048)
+    h_bytes = 8192 * 8 * (2048 // 2 + 2048 // 16)
+    assert full >= stage + h_bytes
+    assert full % 256 == 0 and stage % 256 == 0
+    assert L.moe_ffn_workspace_bytes(-1, 8, 80, 6144, 2048) == 0
+    assert L.moe_route_workspace_bytes(16, 80, 8) > 0
+
+
+def test_stage_validation(L):
+    g = L.moe_nvfp4_gate_up_swiglu
+    assert g(P, P, P, 16, 256, P, P, P, P, 8, 128, 2, P, P, None, P, P2, 1 << 30, None) == NULL
+    assert g(P, P, P, 16, 100, P, P, P, P, 8, 128, 2, P, P, P, P, P2, 1 << 30, None) == SHAPE
+    d = L.moe_nvfp4_down_scatter
+    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, None, P, None, P2, 1 << 30, None) == NULL
+    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, P, P, None, None, 0, None) == WORKSPACE
+
+
+def test_combine_and_reap_validation(L):
+    c = L.moe_combine
+    assert c(None, 4, 2, 64, 0, P, None) == NULL
+    assert c(P, 4, 2, 66, 0, P, None) == SHAPE
+    assert c(P, 4, 2, 64, 2, P, None) == SHAPE
+    assert c(P, 4, 0, 64, 0, P, None) == SHAPE
+    assert c(P, 4, 2, 64, 0, ctypes.c_void_p(0x10004), None) == ALIGN
+    assert c(P, 0, 2, 64, 0, P, None) == OK
+    r = L.reap_saliency
+    assert r(P, P, P, None, 4, 2, 8, P, None) == NULL
+    assert r(P, P, P, P, 4, 2, 0, P, None) == SHAPE
+    assert r(P, P, P, P, 4, 2, 300, P, None) == SHAPE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    from nvfp4_w4a4_mixture_amd import _lib
+
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load(str(tmp_path / "nope.so"))

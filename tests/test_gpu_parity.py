@@ -1,0 +1,274 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle, on seeded inputs.
+
+Bit-exact: NVFP4 codes and scales (activations and weights), top-k ids,
+expert counts/offsets and the permutation.  Tolerances: topk_w within
+1e-6 * rsf, layer output rel-L2 <= 2e-3 (FP32 output against the FP64
+oracle; BF16 output against the oracle rounded to BF16), REAP saliency
+within 1e-3 relative.  Shapes span several tiles with ragged tails, empty
+experts, a single token, k = E, E = 1, and T = 0.
+"""
+
+import json
+import os
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import (bf16_round, check_routing, config_case, dev_bf16, gpu_layer, oracle_codes, oracle_layer,
+                       oracle_perm, random_case, rel_l2, say, to_np)
+from oracle import nvfp4 as onv
+from oracle import routing as oroute
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 2e-3
+SAL_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    from nvfp4_w4a4_mixture_amd import ops as _ops
+
+    return _ops
+
+
+def test_library_loaded_in_tree(ops):
+    path = ops.lib()._name
+    assert os.path.exists(path) and "nvfp4_w4a4_mixture_amd" in path
+    assert ops.lib().moe_abi_version() == 1
+
+
+# ---------------------------------------------------------------------------
+# quantization
+
+def _q_case(rows, cols, dist, seed):
+    rng = np.random.default_rng(seed)
+    if dist == "normal":
+        x = rng.standard_normal((rows, cols))
+    elif dist == "wide":  # per-row magnitudes over 2^-14 .. 2^8: subnormal and saturated block scales
+        x = rng.standard_normal((rows, cols)) * np.exp2(rng.uniform(-14, 8, (rows, 1)))
+    elif dist == "sparse":  # zero blocks and lone values
+        x = rng.standard_normal((rows, cols)) * (rng.random((rows, cols)) < 0.05)
+    elif dist == "ties":  # values on E2M1 decision boundaries for gs such that inv == 1
+        x = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -2.5, 6.0, -6.0], (rows, cols))
+    else:
+        raise ValueError(dist)
+    return gen.f32_to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("rows,cols,dist,gs", [
+    (1, 16, "normal", None), (333, 256, "normal", None), (64, 6144, "normal", None), (257, 512, "wide", None),
+    (100, 128, "sparse", None), (40, 64, "ties", 448.0), (50, 96, "normal", 1e5), (50, 96, "normal", 1e-3)])
+def test_quantize_act_bitexact(ops, rows, cols, dist, gs):
+    say(f"quantize_act rows={rows} cols={cols} dist={dist} gs={gs}")
+    xb = _q_case(rows, cols, dist, rows * 7 + cols)
+    xf = gen.bf16_bits_to_f32(xb)
+    g = np.float32(gs) if gs is not None else onv.global_scale(np.max(np.abs(xf)))
+    codes_ref, scales_ref = onv.quantize(xf, g)
+    codes, scales = ops.nvfp4_quantize_act(dev_bf16(xb), torch.tensor([g], dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(scales), scales_ref)
+    assert np.array_equal(to_np(codes), onv.pack_codes(codes_ref))
+
+
+def test_quantize_act_with_leading_dimension(ops):
+    say("quantize_act ld > cols")
+    xb = _q_case(70, 384, "normal", 5)
+    full = dev_bf16(xb)
+    sub = full[:, 128:384]  # ld = 384, cols = 256, 16-byte aligned start
+    g = np.float32(300.0)
+    codes, scales = ops.nvfp4_quantize_act(sub, torch.tensor([g], dtype=torch.float32, device="cuda"))
+    c_ref, s_ref = onv.quantize(gen.bf16_bits_to_f32(xb[:, 128:384]), g)
+    assert np.array_equal(to_np(scales), s_ref)
+    assert np.array_equal(to_np(codes), onv.pack_codes(c_ref))
+
+
+def test_quantize_act_golden_blocks(ops, golden_dir):
+    with open(os.path.join(golden_dir, "nvfp4_blocks.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        say(f"golden block {case['name']}")
+        xb = gen.f32_to_bf16_bits(np.array([case["x"]], np.float32))
+        g = np.float32(case["gs"])
+        codes, scales = ops.nvfp4_quantize_act(dev_bf16(xb), torch.tensor([g], dtype=torch.float32, device="cuda"))
+        assert int(to_np(scales)[0, 0]) == int(case["scale"], 16), case["name"]
+        assert to_np(codes)[0].tolist() == [int(b, 16) for b in case["packed"]], case["name"]
+
+
+def test_quantize_weights_bitexact(ops):
+    say("quantize_weights batch=3 (one all-zero matrix)")
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((3, 48, 256)).astype(np.float32) * np.array([0.02, 0.0, 0.3], np.float32)[:, None, None]
+    w[2, 5, 7] = 1.5  # a lone outlier sets the third matrix's global scale
+    wb = gen.f32_to_bf16_bits(w)
+    codes, scales, gs = ops.nvfp4_quantize_weights(dev_bf16(wb))
+    torch.cuda.synchronize()
+    for b in range(3):
+        c_ref, s_ref, g_ref = onv.quantize_weight(gen.bf16_bits_to_f32(wb[b]))
+        assert to_np(gs)[b] == g_ref
+        assert np.array_equal(to_np(scales)[b], s_ref)
+        assert np.array_equal(to_np(codes)[b], c_ref)
+    assert to_np(gs)[1] == 1.0
+
+
+# ---------------------------------------------------------------------------
+# routing + permutation
+
+@pytest.mark.parametrize("T,H,E,k", [(64, 256, 8, 2), (300, 512, 80, 8), (1000, 256, 128, 8), (37, 64, 256, 16),
+                                     (5, 32, 1, 1), (3, 32, 16, 16), (2500, 128, 80, 8), (0, 64, 8, 2)])
+def test_route_and_permutation_bitexact(ops, T, H, E, k):
+    say(f"route T={T} H={H} E={E} k={k}")
+    rng = np.random.default_rng(T * 31 + E)
+    xb = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = gen.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    rsf = 2.5
+    out = ops.moe_route(dev_bf16(xb), dev_bf16(wr), torch.from_numpy(bias).cuda(), k, rsf)
+    torch.cuda.synchronize()
+    counts, offsets, perm = to_np(out.expert_counts), to_np(out.expert_offsets), to_np(out.sorted_pair_ids)
+    if T == 0:
+        assert counts.tolist() == [0] * E and offsets.tolist() == [0] * (E + 1)
+        return
+    ids, w = to_np(out.topk_ids), to_np(out.topk_w)
+    ref = dict(zip(("ids", "weights", "weights64", "gap"), oroute.route(xb, wr, bias, k, rsf)))
+    near = check_routing(ids, w, ref, rsf, E)
+    assert near == 0, f"{near} near-tie tokens"
+    c_ref, o_ref, p_ref = oracle_perm(ids, E)
+    assert np.array_equal(counts, c_ref)
+    assert np.array_equal(offsets, o_ref)
+    assert np.array_equal(perm, p_ref)
+
+
+def test_route_exact_ties_go_to_lower_index(ops):
+    say("route crafted ties")
+    H, E, k = 64, 12, 4
+    rng = np.random.default_rng(8)
+    wr = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    wr[5] = wr[2]
+    wr[9] = wr[2]
+    wr[7] = wr[3]
+    wrb = gen.f32_to_bf16_bits(wr)
+    bias = np.zeros(E, np.float32)
+    bias[2] = bias[5] = bias[9] = 2.0  # score > 2 > any other: tied experts 2, 5, 9 lead every token
+    xb = gen.f32_to_bf16_bits(rng.standard_normal((40, H)).astype(np.float32))
+    out = ops.moe_route(dev_bf16(xb), dev_bf16(wrb), torch.from_numpy(bias).cuda(), k, 1.0)
+    ids = to_np(out.topk_ids)
+    ref_ids, _, _, _ = oroute.route(xb, wrb, bias, k, 1.0)
+    assert np.array_equal(ids, ref_ids)
+    assert np.all(ids[:, :3] == [2, 5, 9])
+
+
+# ---------------------------------------------------------------------------
+# whole layer
+
+def _layer_check(ops, case, reap=True):
+    say(f"layer {case.name}: T={case.T} H={case.H} I={case.I} E={case.E} k={case.k}")
+    layer = gpu_layer(case)
+    # weights: GPU RTN == oracle RTN, bitwise
+    c13, s13, g13 = (to_np(t) for t in layer.w13)
+    c2, s2, g2 = (to_np(t) for t in layer.w2)
+    for e, q in enumerate(case.experts_q):
+        assert np.array_equal(c13[e, :case.I], q.gate_codes) and np.array_equal(c13[e, case.I:], q.up_codes)
+        assert np.array_equal(s13[e, :case.I], q.gate_scales) and np.array_equal(s13[e, case.I:], q.up_scales)
+        assert np.array_equal(c2[e], q.down_codes) and np.array_equal(s2[e], q.down_scales)
+        assert g13[e, 0] == q.gate_gs and g13[e, 1] == q.up_gs and g2[e] == q.down_gs
+    x = dev_bf16(case.x)
+    out32 = layer(x, out_dtype=torch.float32, reap=reap)
+    torch.cuda.synchronize()
+    ref = oracle_layer(case, with_pairs=True)
+    ids, w = to_np(out32.route.topk_ids), to_np(out32.route.topk_w)
+    assert check_routing(ids, w, ref, case.rsf, case.E) == 0
+    c_ref, s_ref = oracle_codes(case)
+    assert np.array_equal(to_np(out32.x_codes), c_ref) and np.array_equal(to_np(out32.x_scales), s_ref)
+    y32 = to_np(out32.y)
+    err = rel_l2(y32, ref["y"])
+    pair_ref = ref["pair_f"] * ref["weights64"].reshape(-1)[:, None]
+    perr = rel_l2(to_np(out32.pair_out), pair_ref)
+    print(f"  rel-L2 y(fp32)={err:.3e} pair_out={perr:.3e}", flush=True)
+    assert err <= Y_TOL and perr <= Y_TOL
+    if reap:
+        sal = to_np(out32.saliency).astype(np.float64)
+        cnt = np.bincount(ids.reshape(-1), minlength=case.E)
+        nz = cnt > 0
+        rel = np.abs(sal[nz] - ref["saliency"][nz]) / ref["saliency"][nz]
+        print(f"  saliency max rel={rel.max():.3e}", flush=True)
+        assert rel.max() <= SAL_TOL
+        assert np.all(sal[~nz] == 0.0)
+        sq = to_np(out32.pair_sqnorm).astype(np.float64)
+        assert rel_l2(np.sqrt(sq), ref["pair_norm"]) <= Y_TOL
+    y16 = layer(x, out_dtype=torch.bfloat16, reap=False)
+    torch.cuda.synchronize()
+    err16 = rel_l2(y16.y.float().cpu().numpy(), bf16_round(ref["y"]))
+    print(f"  rel-L2 y(bf16 vs bf16(ref))={err16:.3e}", flush=True)
+    assert err16 <= Y_TOL
+    return layer, out32, ref
+
+
+def test_layer_parity_config0(ops):
+    _layer_check(ops, config_case(CONFIGS[0]))
+
+
+@pytest.mark.parametrize("name,T,H,I,E,k", [
+    ("ragged_tiles", 300, 512, 256, 8, 2),
+    ("multi_mtile", 300, 256, 128, 3, 2),
+    ("decode_small", 16, 512, 256, 16, 4),
+    ("single_token", 1, 256, 128, 8, 2),
+    ("dense_e1_k1", 20, 256, 128, 1, 1),
+    ("k_equals_e", 17, 256, 128, 4, 4),
+    ("many_empty_experts", 40, 256, 128, 256, 8),
+    ("tiled_mid", 130, 768, 384, 6, 3),
+])
+def test_layer_parity_random(ops, name, T, H, I, E, k):
+    case = random_case(name, zlib.crc32(name.encode()) % 1000, T, H, I, E, k)
+    _layer_check(ops, case)
+
+
+def test_single_expert_output_is_rsf_times_mlp(ops):
+    case = random_case("e1", 11, 24, 256, 128, 1, 1)
+    layer, out, ref = _layer_check(ops, case, reap=False)
+    assert np.all(to_np(out.route.topk_w) == np.float32(case.rsf))
+
+
+@pytest.mark.parametrize("T", [150, 12])  # tiled path, small-M path
+def test_grouped_ffn_matches_stage_calls(ops, T):
+    case = random_case(f"stages{T}", 5, T, 256, 128, 5, 2)
+    say(f"grouped ffn vs stage entry points T={T}")
+    layer = gpu_layer(case)
+    x = dev_bf16(case.x)
+    out = layer(x, out_dtype=torch.float32, reap=True)  # the layer calls the two stage entry points
+    r = out.route
+    pair_out, sq = ops.moe_nvfp4_grouped_ffn(out.x_codes, out.x_scales, layer.x_gs, *layer.w13, *layer.w2,
+                                             layer.h_gs, case.k, r.expert_offsets, r.sorted_pair_ids, r.topk_w,
+                                             pair_sqnorm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pair_out, out.pair_out)
+    assert torch.equal(sq, out.pair_sqnorm)
+
+
+def test_zero_tokens_is_a_noop(ops):
+    say("T = 0")
+    case = random_case("t0", 2, 4, 256, 128, 4, 2)
+    layer = gpu_layer(case)
+    x = torch.empty((0, case.H), dtype=torch.bfloat16, device="cuda")
+    out = layer(x, out_dtype=torch.float32, reap=True)
+    torch.cuda.synchronize()
+    assert out.y.shape == (0, case.H)
+    assert torch.all(out.route.expert_counts == 0)
+    assert torch.all(out.saliency == 0)
+
+
+def test_repeat_runs_are_bitwise_identical(ops):
+    case = random_case("determinism", 9, 200, 256, 128, 8, 2)
+    say("determinism")
+    layer = gpu_layer(case)
+    x = dev_bf16(case.x)
+    a = layer(x, out_dtype=torch.float32, reap=True)
+    ya, sa, pa = a.y.clone(), a.saliency.clone(), a.route.sorted_pair_ids.clone()
+    b = layer(x, out_dtype=torch.float32, reap=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, b.y) and torch.equal(sa, b.saliency) and torch.equal(pa, b.route.sorted_pair_ids)
