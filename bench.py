@@ -42,7 +42,22 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = decode-shaped layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) to calibrate HBM counters")
     return ap.parse_args(argv)
+
+
+def copy_probe(mib: int) -> int:
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "copies": 3}), flush=True)
+    return 0
 
 
 def ffn_source_hash() -> str:
@@ -134,9 +149,11 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this layer build runs on exactly one GPU; --gpus must be 1 "
-                                   "(multi-GPU expert sharding is described in DESIGN.md, not built)"}), flush=True)
+        print(json.dumps({"error": "this layer runs on exactly one GPU; --gpus must be 1 "
+                                   "(expert-parallel sharding over several GPUs is not built)"}), flush=True)
         return 2
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
     import numpy as np
     import torch
 

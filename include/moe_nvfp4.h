@@ -96,9 +96,9 @@ int32_t moe_abi_version(void);
  *
  * x_bf16 [T, ldx] (row-major, ldx >= H); w_router_bf16 [E, H]; bias [E]
  * FP32; 1 <= k <= E <= 256; T * k < 2^31; routed_scaling_factor > 0.
- * workspace: at least moe_route_workspace_bytes(T, E, k) bytes, 256-byte
+ * workspace: at least moe_route_workspace_bytes(T, H, E, k) bytes, 256-byte
  * aligned, device memory; its contents on entry do not matter. */
-size_t moe_route_workspace_bytes(int64_t T, int64_t E, int64_t k);
+size_t moe_route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k);
 moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
                      const uint16_t* w_router_bf16, const float* bias, int64_t E, int64_t k,
                      float routed_scaling_factor, int32_t* topk_ids, float* topk_w,

@@ -29,7 +29,7 @@ _sz = ctypes.c_size_t
 SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (_i32, []),
-    "moe_route_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "moe_route_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "moe_route": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "nvfp4_quantize_act": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "nvfp4_quantize_weights": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),

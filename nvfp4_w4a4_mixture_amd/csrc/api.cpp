@@ -102,9 +102,9 @@ const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 int32_t moe_abi_version(void) { return MOE_NVFP4_ABI_VERSION; }
 
-size_t moe_route_workspace_bytes(int64_t T, int64_t E, int64_t k) {
-  if (T < 0 || E < 1 || k < 1) return 0;
-  return moe::route_workspace_bytes(T, E, k);
+size_t moe_route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k) {
+  if (T < 0 || H < 1 || E < 1 || k < 1) return 0;
+  return moe::route_workspace_bytes(T, H, E, k);
 }
 
 moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx, const uint16_t* w_router_bf16,
@@ -118,7 +118,7 @@ moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx, 
   if (k < 1 || E < k || E > 256) return fail(MOE_ERR_SHAPE, "moe_route: need 1 <= k <= E <= 256");
   if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "moe_route: T*k must be < 2^31");
   if (!(routed_scaling_factor > 0.0f)) return fail(MOE_ERR_SHAPE, "moe_route: routed_scaling_factor must be > 0");
-  const size_t need = moe::route_workspace_bytes(T, E, k);
+  const size_t need = moe::route_workspace_bytes(T, H, E, k);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MOE_ERR_WORKSPACE, "moe_route: workspace needs %zu bytes", need);
   if (need > 0 && !aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "moe_route: workspace must be 256-byte aligned");

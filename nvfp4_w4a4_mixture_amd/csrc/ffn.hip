@@ -19,9 +19,11 @@
 //
 // Two kernels:
 //  * ffn_small_kernel (decode batches, every expert has <= 16 pairs): one
-//    workgroup per (expert, 64-row weight tile); the four waves interleave
-//    over 128-element K chunks; weights go straight from HBM to registers
-//    (each weight byte is used once), 16x16x32 MFMA; partial sums meet in LDS.
+//    workgroup per (expert, 64-row weight tile); each of the four waves takes
+//    a contiguous quarter of K in 256-element iterations (a full 128-byte line
+//    per weight row), prefetching the next iteration into registers; weights
+//    go straight from HBM to registers (each weight byte is used once),
+//    16x16x32 MFMA; the waves' partial sums meet in LDS.
 //  * ffn_tiled_kernel (any M): one workgroup per (m-tile of an expert's
 //    pairs, n-tile of weight rows); A and B FP4 tiles staged through
 //    double-buffered LDS, 32x32x16 MFMA, 2x2 waves.
@@ -37,8 +39,27 @@ enum { kGateUp = 0, kDown = 1 };
 
 constexpr int kSmallRows = 16;  // pairs per expert handled (M_e <= 16)
 
-template <int MODE>
+// Per-lane operand data of one K iteration (KB logical k per row; each lane
+// group of 16 lanes takes KB/4 contiguous k: KB/8 code bytes, KB/64 scales).
+template <int KB>
+struct SmallIter {
+  static constexpr int kDw = KB / 32;  // code dwords per lane = MFMA k-steps
+  u32x4_t ac[kDw / 4];
+  uint32_t as;
+  u32x4_t bc[4][kDw / 4];
+  uint32_t bs[4];
+};
+
+template <int KB>
+__device__ __forceinline__ uint32_t load_scales(const uint8_t* p) {
+  if (KB == 256) return *reinterpret_cast<const uint32_t*>(p);
+  return *reinterpret_cast<const uint16_t*>(p);
+}
+
+template <int MODE, int KB>
 __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
+  using It = SmallIter<KB>;
+  constexpr int kDw = It::kDw;
   const int tile = blockIdx.x;
   const int e = blockIdx.y;
   const int off = a.offsets[e];
@@ -51,17 +72,10 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
 
   // A row (pair c of this expert)
   const bool a_valid = c < Me;
-  const uint8_t* a_code_row;
-  const uint8_t* a_scale_row;
-  {
-    int64_t arow = 0;
-    if (a_valid) {
-      if (MODE == kGateUp) arow = a.sorted[off + c] / a.k;
-      else arow = off + c;
-    }
-    a_code_row = a.a_codes + arow * kbytes;
-    a_scale_row = a.a_scales + arow * kscales;
-  }
+  int64_t arow = 0;
+  if (a_valid) arow = (MODE == kGateUp) ? (int64_t)(a.sorted[off + c] / a.k) : (int64_t)(off + c);
+  const uint8_t* a_code_row = a.a_codes + arow * kbytes + g * (KB / 8);
+  const uint8_t* a_scale_row = a.a_scales + arow * kscales + g * (KB / 64);
   // B rows for the 4 n-subtiles of 16 rows
   const uint8_t* b_code_row[4];
   const uint8_t* b_scale_row[4];
@@ -74,40 +88,52 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
     } else {
       brow = (int64_t)e * a.H + (int64_t)tile * 64 + 16 * j + c;
     }
-    b_code_row[j] = a.b_codes + brow * kbytes;
-    b_scale_row[j] = a.b_scales + brow * kscales;
+    b_code_row[j] = a.b_codes + brow * kbytes + g * (KB / 8);
+    b_scale_row[j] = a.b_scales + brow * kscales + g * (KB / 64);
   }
+
+  auto load = [&](int64_t it, It& d) {
+    const int64_t cb = it * (KB / 2), sb = it * (KB / 16);
+#pragma unroll
+    for (int q = 0; q < kDw / 4; ++q)
+      d.ac[q] = a_valid ? *reinterpret_cast<const u32x4_t*>(a_code_row + cb + 16 * q) : u32x4_t{0, 0, 0, 0};
+    d.as = a_valid ? load_scales<KB>(a_scale_row + sb) : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int q = 0; q < kDw / 4; ++q)
+        d.bc[j][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b_code_row[j] + cb + 16 * q));
+      d.bs[j] = load_scales<KB>(b_scale_row[j] + sb);
+    }
+  };
 
   float4_t acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int64_t nchunks = K / 128;
-  for (int64_t ch = wave; ch < nchunks; ch += 4) {
-    const int64_t cb = ch * 64 + 16 * g;  // code byte offset of this lane's 32 codes
-    const int64_t sb = ch * 8 + 2 * g;    // scale byte offset of its 2 blocks
-    uint4 ac = make_uint4(0, 0, 0, 0);
-    uint32_t as = 0;
-    if (a_valid) {
-      ac = *reinterpret_cast<const uint4*>(a_code_row + cb);
-      as = *reinterpret_cast<const uint16_t*>(a_scale_row + sb);
-    }
-    u32x4_t bc[4];
-    uint32_t bs[4];
+  auto compute = [&](const It& d) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bc[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b_code_row[j] + cb));
-      bs[j] = *reinterpret_cast<const uint16_t*>(b_scale_row[j] + sb);
-    }
-    const uint32_t acw[4] = {ac.x, ac.y, ac.z, ac.w};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const half8_t af = decode8(acw[s], scale_pair((as >> (8 * (s >> 1))) & 0xFFu));
+    for (int s = 0; s < kDw; ++s) {
+      const int sbyte = s >> 1;  // two dwords (16 codes) per scale block
+      const half8_t af = decode8(d.ac[s >> 2][s & 3], scale_pair((d.as >> (8 * sbyte)) & 0xFFu));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const half8_t bf = decode8(bc[j][s], scale_pair((bs[j] >> (8 * (s >> 1))) & 0xFFu));
+        const half8_t bf = decode8(d.bc[j][s >> 2][s & 3], scale_pair((d.bs[j] >> (8 * sbyte)) & 0xFFu));
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[j], 0, 0, 0);
       }
+    }
+  };
+
+  // each wave takes a contiguous range of K iterations; the next iteration's
+  // loads are in flight while the current one is decoded and multiplied
+  const int64_t nit = K / KB;
+  const int64_t it0 = (wave * nit) / 4, it1 = ((wave + 1) * nit) / 4;
+  if (it0 < it1) {
+    It cur, nxt;
+    load(it0, cur);
+    for (int64_t it = it0; it < it1; ++it) {
+      if (it + 1 < it1) load(it + 1, nxt);
+      compute(cur);
+      cur = nxt;
     }
   }
 
@@ -452,7 +478,8 @@ __global__ void sq_reduce_kernel(const float* __restrict__ part, int64_t npairs,
   const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= npairs) return;
   float s = 0.0f;
-  for (int i = 0; i < n_part; ++i) s += part[p * n_part + i];
+#pragma unroll 8
+  for (int i = 0; i < n_part; ++i) s += part[p * n_part + i];  // fixed order
   out[p] = s;
 }
 
@@ -468,10 +495,14 @@ bool ffn_use_small(int64_t T) { return T <= kSmallRows; }
 
 hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool build_schedule, hipStream_t st) {
   if (ffn_use_small(T)) {
+    const bool k256 = (a.K % 256) == 0;  // else K % 128 == 0
+    const dim3 grid = mode == kGateUp ? dim3((unsigned)(a.I / 32), (unsigned)E) : dim3((unsigned)(a.H / 64), (unsigned)E);
     if (mode == kGateUp) {
-      hipLaunchKernelGGL(ffn_small_kernel<kGateUp>, dim3((unsigned)(a.I / 32), (unsigned)E), dim3(256), 0, st, a);
+      if (k256) hipLaunchKernelGGL((ffn_small_kernel<kGateUp, 256>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((ffn_small_kernel<kGateUp, 128>), grid, dim3(256), 0, st, a);
     } else {
-      hipLaunchKernelGGL(ffn_small_kernel<kDown>, dim3((unsigned)(a.H / 64), (unsigned)E), dim3(256), 0, st, a);
+      if (k256) hipLaunchKernelGGL((ffn_small_kernel<kDown, 256>), grid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((ffn_small_kernel<kDown, 128>), grid, dim3(256), 0, st, a);
     }
     return hipGetLastError();
   }

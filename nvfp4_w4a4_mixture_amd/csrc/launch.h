@@ -39,7 +39,7 @@ hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, i
 hipError_t launch_weight_global_scales(const uint16_t* w, int64_t batch, int64_t per_matrix, float* gs,
                                        hipStream_t stream);
 
-size_t route_workspace_bytes(int64_t T, int64_t E, int64_t k);
+size_t route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k);
 hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, const float* bias,
                         int64_t E, int64_t k, float rsf, int32_t* topk_ids, float* topk_w, int32_t* counts,
                         int32_t* offsets, int32_t* sorted, void* workspace, hipStream_t st);

@@ -67,7 +67,7 @@ class NVFP4MoELayer:
                                    torch.empty((E,), dtype=torch.int32, device=d),
                                    torch.empty((E + 1,), dtype=torch.int32, device=d),
                                    torch.empty((T * k,), dtype=torch.int32, device=d)),
-                route_ws=torch.empty((max(ops.moe_route_workspace_bytes(T, E, k), 1),), dtype=torch.uint8, device=d),
+                route_ws=torch.empty((max(ops.moe_route_workspace_bytes(T, H, E, k), 1),), dtype=torch.uint8, device=d),
                 x_codes=torch.empty((T, H // 2), dtype=torch.uint8, device=d),
                 x_scales=torch.empty((T, H // 16), dtype=torch.uint8, device=d),
                 pair_out=torch.empty((T * k, H), dtype=torch.float32, device=d),

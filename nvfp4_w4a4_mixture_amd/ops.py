@@ -49,8 +49,8 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def moe_route_workspace_bytes(T: int, E: int, k: int) -> int:
-    return int(lib().moe_route_workspace_bytes(T, E, k))
+def moe_route_workspace_bytes(T: int, H: int, E: int, k: int) -> int:
+    return int(lib().moe_route_workspace_bytes(T, H, E, k))
 
 
 def moe_ffn_workspace_bytes(T: int, k: int, E: int, H: int, I: int) -> int:
@@ -87,7 +87,7 @@ def moe_route(x_bf16: torch.Tensor, w_router_bf16: torch.Tensor, bias: torch.Ten
                        torch.empty((E,), dtype=torch.int32, device=dev),
                        torch.empty((E + 1,), dtype=torch.int32, device=dev),
                        torch.empty((T * k,), dtype=torch.int32, device=dev))
-    nbytes = moe_route_workspace_bytes(T, E, k)
+    nbytes = moe_route_workspace_bytes(T, H, E, k)
     ws = _workspace(nbytes, dev, workspace)
     st = lib().moe_route(_p(x_bf16), T, H, ldx, _p(w_router_bf16), _p(bias), E, k,
                          float(routed_scaling_factor), _p(out.topk_ids), _p(out.topk_w), _p(out.expert_counts),

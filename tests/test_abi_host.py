@@ -117,7 +117,7 @@ def test_ffn_workspace_queries(L):
     assert full >= stage + h_bytes
     assert full % 256 == 0 and stage % 256 == 0
     assert L.moe_ffn_workspace_bytes(-1, 8, 80, 6144, 2048) == 0
-    assert L.moe_route_workspace_bytes(16, 80, 8) > 0
+    assert L.moe_route_workspace_bytes(16, 6144, 80, 8) > 0
 
 
 def test_stage_validation(L):
