@@ -32,30 +32,32 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``lib/libmoe_nvfp4.so``; returns its path."""
+def build(verbose: bool = False, out_dir: str = OUT_DIR, build_dir: str = BUILD_DIR, defines=()) -> str:
+    """Compile every source and link ``<out_dir>/libmoe_nvfp4.so``; returns its path.
+
+    ``defines`` (NAME=VALUE strings) override compile-time tile parameters."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(OUT_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = os.path.join(OUT_DIR, LIB_NAME + ".tmp")
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = os.path.join(out_dir, LIB_NAME + ".tmp")
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    out = os.path.join(OUT_DIR, LIB_NAME)
+    out = os.path.join(out_dir, LIB_NAME)
     shutil.move(tmp, out)
     if verbose:
         print("built", out)

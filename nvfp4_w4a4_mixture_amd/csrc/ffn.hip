@@ -25,8 +25,11 @@
 //    go straight from HBM to registers (each weight byte is used once),
 //    16x16x32 MFMA; the waves' partial sums meet in LDS.
 //  * ffn_tiled_kernel (any M): one workgroup per (m-tile of an expert's
-//    pairs, n-tile of weight rows); A and B FP4 tiles staged through
-//    double-buffered LDS, 32x32x16 MFMA, 2x2 waves.
+//    pairs, n-tile of weight rows); A and B FP4 tiles go from HBM straight
+//    into a ring of LDS stages (global_load_lds, no register staging) that
+//    keeps several stages in flight; 32x32x16 MFMA, 2x2 waves of 128x128
+//    each (16 accumulator tiles per wave: 8 decoded fragments feed 16 MFMAs
+//    per k-step).
 #include "device_common.h"
 #include "launch.h"
 
@@ -70,10 +73,11 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
   const int64_t K = a.K;
   const int64_t kbytes = K / 2, kscales = K / 16;
 
-  // A row (pair c of this expert)
+  // A row (pair c of this expert); rows past M_e read row off's data with a
+  // zero scale, so they decode to zeros without a branch
   const bool a_valid = c < Me;
-  int64_t arow = 0;
-  if (a_valid) arow = (MODE == kGateUp) ? (int64_t)(a.sorted[off + c] / a.k) : (int64_t)(off + c);
+  const int cc = a_valid ? c : 0;
+  const int64_t arow = (MODE == kGateUp) ? (int64_t)(a.sorted[off + cc] / a.k) : (int64_t)(off + cc);
   const uint8_t* a_code_row = a.a_codes + arow * kbytes + g * (KB / 8);
   const uint8_t* a_scale_row = a.a_scales + arow * kscales + g * (KB / 64);
   // B rows for the 4 n-subtiles of 16 rows
@@ -95,8 +99,7 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
   auto load = [&](int64_t it, It& d) {
     const int64_t cb = it * (KB / 2), sb = it * (KB / 16);
 #pragma unroll
-    for (int q = 0; q < kDw / 4; ++q)
-      d.ac[q] = a_valid ? *reinterpret_cast<const u32x4_t*>(a_code_row + cb + 16 * q) : u32x4_t{0, 0, 0, 0};
+    for (int q = 0; q < kDw / 4; ++q) d.ac[q] = *reinterpret_cast<const u32x4_t*>(a_code_row + cb + 16 * q);
     d.as = a_valid ? load_scales<KB>(a_scale_row + sb) : 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -114,10 +117,10 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
 #pragma unroll
     for (int s = 0; s < kDw; ++s) {
       const int sbyte = s >> 1;  // two dwords (16 codes) per scale block
-      const half8_t af = decode8(d.ac[s >> 2][s & 3], scale_pair((d.as >> (8 * sbyte)) & 0xFFu));
+      const half8_t af = decode8(d.ac[s >> 2][s & 3], scale_pair(d.as, sbyte));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const half8_t bf = decode8(d.bc[j][s >> 2][s & 3], scale_pair((d.bs[j] >> (8 * sbyte)) & 0xFFu));
+        const half8_t bf = decode8(d.bc[j][s >> 2][s & 3], scale_pair(d.bs[j], sbyte));
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[j], 0, 0, 0);
       }
     }
@@ -202,24 +205,50 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
 // ---------------------------------------------------------------------------
 // tiled kernel
 
-template <int WM, int WN>
+template <int WM, int WN, int NS>
 struct TiledShape {
   static constexpr int BM = 64 * WM;  // 2 waves in M, WM 32-row MFMA tiles each
   static constexpr int BN = 64 * WN;  // 2 waves in N, WN 32-col MFMA tiles each
-  static constexpr int kACodeBytes = 4 * BM * 16;  // [chunk 4][row][16 B]
-  static constexpr int kAScaleBytes = 2 * BM * 4;  // [group 2][row][4 B]
-  static constexpr int kBCodeBytes = 4 * BN * 16;
-  static constexpr int kBScaleBytes = 2 * BN * 4;
+  // codes: [row][4 slots of 16 B], chunk c of row r in slot c ^ ((r >> 2) & 3):
+  // 16 lanes reading one chunk of 16 consecutive rows, and the 16 lanes of a
+  // DMA group writing the 4 chunks of 4 consecutive rows, each touch 16
+  // distinct 16-byte bank groups (64 banks); scales: [row][8 B]
+  static constexpr int kACodeBytes = BM * 64;
+  static constexpr int kAScaleBytes = BM * 8;
+  static constexpr int kBCodeBytes = BN * 64;
+  static constexpr int kBScaleBytes = BN * 8;
   static constexpr int kStage = kACodeBytes + kAScaleBytes + kBCodeBytes + kBScaleBytes;
   static constexpr int kHcols = BN / 2;             // gate_up: h columns per tile
   static constexpr int kHStride = kHcols + 4;       // floats per LDS row of h
   static constexpr int kHBytes = BM * kHStride * 4;
-  static constexpr int kLds = (2 * kStage > kHBytes ? 2 * kStage : kHBytes) + 2 * BM * 4;
+  static constexpr int kLds = (NS * kStage > kHBytes ? NS * kStage : kHBytes) + 2 * BM * 4;
+  // DMA instructions per wave per stage (4 waves): 16-byte code loads cover 16
+  // rows, 4-byte scale loads cover 32 rows
+  static constexpr int kACodeOps = BM / 64, kAScaleOps = BM / 128;
+  static constexpr int kBCodeOps = BN / 64, kBScaleOps = BN / 128;
+  static constexpr int kLoadsPerStage = kACodeOps + kAScaleOps + kBCodeOps + kBScaleOps;
 };
 
-template <int MODE, int WM, int WN>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int MODE, int WM, int WN, int NS>
 __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
-  using S = TiledShape<WM, WN>;
+  using S = TiledShape<WM, WN, NS>;
   constexpr int BM = S::BM, BN = S::BN;
   const int nt = blockIdx.x;
   const int mt = blockIdx.y;
@@ -235,32 +264,12 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
   const int r = lane & 31, g = lane >> 5;
   const int64_t K = a.K, kbytes = K / 2, kscales = K / 16;
 
-  // ---- per-thread global sources
-  // A codes: row = (tid >> 2) + 64 * i, chunk = tid & 3
-  constexpr int kARowsPerThread = BM / 64;
-  const uint8_t* a_code_src[kARowsPerThread];
-  bool a_ok[kARowsPerThread];
-#pragma unroll
-  for (int i = 0; i < kARowsPerThread; ++i) {
-    const int m = (tid >> 2) + 64 * i;
-    a_ok[i] = m < rows_here;
-    int64_t arow = 0;
-    if (a_ok[i]) arow = (MODE == kGateUp) ? (int64_t)(a.sorted[off + row0 + m] / a.k) : (int64_t)(off + row0 + m);
-    a_code_src[i] = a.a_codes + arow * kbytes + 16 * (tid & 3);
-  }
-  // A scales: row = (tid >> 1) + 128 * i, dword = tid & 1
-  constexpr int kAScalePerThread = (BM * 2 + 255) / 256;
-  const uint8_t* a_scale_src[kAScalePerThread];
-  bool as_ok[kAScalePerThread];
-#pragma unroll
-  for (int i = 0; i < kAScalePerThread; ++i) {
-    const int m = (tid >> 1) + 128 * i;
-    as_ok[i] = m < rows_here && m < BM;
-    int64_t arow = 0;
-    if (as_ok[i]) arow = (MODE == kGateUp) ? (int64_t)(a.sorted[off + row0 + m] / a.k) : (int64_t)(off + row0 + m);
-    a_scale_src[i] = a.a_scales + arow * kscales + 4 * (tid & 1);
-  }
-  // B rows
+  // ---- per-lane DMA sources.  Rows past rows_here read the tile's first row:
+  // their MFMA output rows are never stored.
+  auto a_row = [&](int m) -> int64_t {
+    const int mm = m < rows_here ? m : 0;
+    return (MODE == kGateUp) ? (int64_t)(a.sorted[off + row0 + mm] / a.k) : (int64_t)(off + row0 + mm);
+  };
   auto b_row = [&](int n) -> int64_t {
     if (MODE == kGateUp) {
       const int wv = n / (32 * WN), j = (n % (32 * WN)) / 32, cc = n % 32;
@@ -270,52 +279,49 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
       return (int64_t)e * a.H + (int64_t)nt * BN + n;
     }
   };
-  constexpr int kBRowsPerThread = BN / 64;
-  const uint8_t* b_code_src[kBRowsPerThread];
+  // 16-byte code DMA i of this wave: rows 16 q .. 16 q + 15 with q = 4 i + wave;
+  // lane -> row 16 q + lane / 4, LDS slot lane % 4 holding chunk slot ^ ((row >> 2) & 3)
+  const uint8_t* a_code_src[S::kACodeOps];
+  const uint8_t* b_code_src[S::kBCodeOps];
 #pragma unroll
-  for (int i = 0; i < kBRowsPerThread; ++i) b_code_src[i] = a.b_codes + b_row((tid >> 2) + 64 * i) * kbytes + 16 * (tid & 3);
-  constexpr int kBScalePerThread = (BN * 2 + 255) / 256;
-  const uint8_t* b_scale_src[kBScalePerThread];
-  bool bs_ok[kBScalePerThread];
+  for (int i = 0; i < S::kACodeOps; ++i) {
+    const int row = 16 * (4 * i + wave) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    a_code_src[i] = a.a_codes + a_row(row) * kbytes + 16 * chunk;
+  }
 #pragma unroll
-  for (int i = 0; i < kBScalePerThread; ++i) {
-    const int n = (tid >> 1) + 128 * i;
-    bs_ok[i] = n < BN;
-    b_scale_src[i] = a.b_scales + b_row(bs_ok[i] ? n : 0) * kscales + 4 * (tid & 1);
+  for (int i = 0; i < S::kBCodeOps; ++i) {
+    const int row = 16 * (4 * i + wave) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    b_code_src[i] = a.b_codes + b_row(row) * kbytes + 16 * chunk;
+  }
+  // 4-byte scale DMA i of this wave: rows 32 q .. 32 q + 31, q = 4 i + wave; lane -> row 32 q + lane / 2, dword lane % 2
+  const uint8_t* a_scale_src[S::kAScaleOps];
+  const uint8_t* b_scale_src[S::kBScaleOps];
+#pragma unroll
+  for (int i = 0; i < S::kAScaleOps; ++i) {
+    const int row = 32 * (4 * i + wave) + (lane >> 1);
+    a_scale_src[i] = a.a_scales + a_row(row) * kscales + 4 * (lane & 1);
+  }
+#pragma unroll
+  for (int i = 0; i < S::kBScaleOps; ++i) {
+    const int row = 32 * (4 * i + wave) + (lane >> 1);
+    b_scale_src[i] = a.b_scales + b_row(row) * kscales + 4 * (lane & 1);
   }
 
-  uint4 ra[kARowsPerThread], rb[kBRowsPerThread];
-  uint32_t ras[kAScalePerThread], rbs[kBScalePerThread];
-  auto gload = [&](int64_t k0) {
-    const int64_t cbo = k0 / 2, sbo = k0 / 16;
+  auto issue = [&](int64_t st) {
+    unsigned char* base = smem + (int)(st % NS) * S::kStage;
+    const int64_t cbo = st * 64, sbo = st * 8;  // 128 k per stage
 #pragma unroll
-    for (int i = 0; i < kARowsPerThread; ++i)
-      ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_code_src[i] + cbo) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < S::kACodeOps; ++i) dma16(a_code_src[i] + cbo, base + (4 * i + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < kAScalePerThread; ++i)
-      ras[i] = as_ok[i] ? *reinterpret_cast<const uint32_t*>(a_scale_src[i] + sbo) : 0u;
+    for (int i = 0; i < S::kAScaleOps; ++i) dma4(a_scale_src[i] + sbo, base + S::kACodeBytes + (4 * i + wave) * 256);
 #pragma unroll
-    for (int i = 0; i < kBRowsPerThread; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_code_src[i] + cbo);
+    for (int i = 0; i < S::kBCodeOps; ++i)
+      dma16(b_code_src[i] + cbo, base + S::kACodeBytes + S::kAScaleBytes + (4 * i + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < kBScalePerThread; ++i)
-      rbs[i] = bs_ok[i] ? *reinterpret_cast<const uint32_t*>(b_scale_src[i] + sbo) : 0u;
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* base = smem + buf * S::kStage;
-    uint4* ac = reinterpret_cast<uint4*>(base);
-    uint32_t* as = reinterpret_cast<uint32_t*>(base + S::kACodeBytes);
-    uint4* bc = reinterpret_cast<uint4*>(base + S::kACodeBytes + S::kAScaleBytes);
-    uint32_t* bsc = reinterpret_cast<uint32_t*>(base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes);
-#pragma unroll
-    for (int i = 0; i < kARowsPerThread; ++i) ac[(tid & 3) * BM + (tid >> 2) + 64 * i] = ra[i];
-#pragma unroll
-    for (int i = 0; i < kAScalePerThread; ++i)
-      if ((tid >> 1) + 128 * i < BM) as[(tid & 1) * BM + (tid >> 1) + 128 * i] = ras[i];
-#pragma unroll
-    for (int i = 0; i < kBRowsPerThread; ++i) bc[(tid & 3) * BN + (tid >> 2) + 64 * i] = rb[i];
-#pragma unroll
-    for (int i = 0; i < kBScalePerThread; ++i)
-      if (bs_ok[i]) bsc[(tid & 1) * BN + (tid >> 1) + 128 * i] = rbs[i];
+    for (int i = 0; i < S::kBScaleOps; ++i)
+      dma4(b_scale_src[i] + sbo, base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes + (4 * i + wave) * 256);
   };
 
   float16_t acc[WM][WN];
@@ -326,30 +332,45 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+  // NS-stage ring: stages st+1 .. st+NS-2 stay in flight while stage st is
+  // consumed; one barrier per stage both publishes stage st and frees the
+  // buffer of stage st-1 for the next DMA.
   const int64_t nst = K / 128;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nst) issue(p);
   for (int64_t st = 0; st < nst; ++st) {
-    const int buf = (int)(st & 1);
-    if (st + 1 < nst) gload((st + 1) * 128);
-    const unsigned char* base = smem + buf * S::kStage;
+    const int64_t ahead = nst - 1 - st;  // stages issued after st that may still be in flight
+    if (ahead >= NS - 2) wait_vmcnt<S::kLoadsPerStage * (NS - 2)>();
+    else if (NS >= 4 && ahead == 2) wait_vmcnt<S::kLoadsPerStage * 2>();
+    else if (NS >= 3 && ahead == 1) wait_vmcnt<S::kLoadsPerStage>();
+    else wait_vmcnt<0>();
+    // Bare s_barrier: this wave's DMA for stage st has landed (vmcnt above), and
+    // its reads of stage st-1's buffer were consumed in the previous iteration.
+    // __syncthreads() would also wait for every DMA still in flight.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const unsigned char* base = smem + (int)(st % NS) * S::kStage;
     const uint4* ac = reinterpret_cast<const uint4*>(base);
     const uint32_t* as = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes);
     const uint4* bc = reinterpret_cast<const uint4*>(base + S::kACodeBytes + S::kAScaleBytes);
     const uint32_t* bsc = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes);
     uint32_t sa[WM], sbv[WN];
 #pragma unroll
-    for (int i = 0; i < WM; ++i) sa[i] = as[g * BM + wm * 32 * WM + 32 * i + r];
+    for (int i = 0; i < WM; ++i) sa[i] = as[(wm * 32 * WM + 32 * i + r) * 2 + g];
 #pragma unroll
-    for (int j = 0; j < WN; ++j) sbv[j] = bsc[g * BN + wn * 32 * WN + 32 * j + r];
+    for (int j = 0; j < WN; ++j) sbv[j] = bsc[(wn * 32 * WN + 32 * j + r) * 2 + g];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint4 ca[WM], cbq[WN];
+      // rows below are r + multiples of 32, so (row >> 2) & 3 == (r >> 2) & 3
+      const int slot = (2 * g + q) ^ ((r >> 2) & 3);
 #pragma unroll
-      for (int i = 0; i < WM; ++i) ca[i] = ac[(2 * g + q) * BM + wm * 32 * WM + 32 * i + r];
+      for (int i = 0; i < WM; ++i) ca[i] = ac[(wm * 32 * WM + 32 * i + r) * 4 + slot];
 #pragma unroll
-      for (int j = 0; j < WN; ++j) cbq[j] = bc[(2 * g + q) * BN + wn * 32 * WN + 32 * j + r];
+      for (int j = 0; j < WN; ++j) cbq[j] = bc[(wn * 32 * WN + 32 * j + r) * 4 + slot];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int sbyte = 2 * q + (s >> 1);
@@ -357,12 +378,12 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 #pragma unroll
         for (int i = 0; i < WM; ++i) {
           const uint32_t w = s == 0 ? ca[i].x : s == 1 ? ca[i].y : s == 2 ? ca[i].z : ca[i].w;
-          af[i] = decode8(w, scale_pair((sa[i] >> (8 * sbyte)) & 0xFFu));
+          af[i] = decode8(w, scale_pair(sa[i], sbyte));
         }
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const uint32_t w = s == 0 ? cbq[j].x : s == 1 ? cbq[j].y : s == 2 ? cbq[j].z : cbq[j].w;
-          bf[j] = decode8(w, scale_pair((sbv[j] >> (8 * sbyte)) & 0xFFu));
+          bf[j] = decode8(w, scale_pair(sbv[j], sbyte));
         }
 #pragma unroll
         for (int i = 0; i < WM; ++i)
@@ -370,9 +391,8 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
           for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (st + 1 < nst) lstore(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done with the ring before the epilogue reuses the LDS
 
   // ---- epilogues.  acc[i][j][q]: row = wm*32*WM + 32 i + 8 (q/4) + 4 g + q%4, col = r
   if (MODE == kGateUp) {
@@ -486,8 +506,17 @@ __global__ void sq_reduce_kernel(const float* __restrict__ part, int64_t npairs,
 // ---------------------------------------------------------------------------
 // host side
 
-constexpr int kTiledWM = 2, kTiledWN = 2;
-using Tiled = TiledShape<kTiledWM, kTiledWN>;
+#ifndef MOE_TILED_WM
+#define MOE_TILED_WM 4
+#endif
+#ifndef MOE_TILED_WN
+#define MOE_TILED_WN 4
+#endif
+#ifndef MOE_TILED_NS
+#define MOE_TILED_NS 4
+#endif
+constexpr int kTiledWM = MOE_TILED_WM, kTiledWN = MOE_TILED_WN, kTiledNS = MOE_TILED_NS;
+using Tiled = TiledShape<kTiledWM, kTiledWN, kTiledNS>;
 
 int64_t ffn_max_tiles(int64_t T, int64_t k, int64_t E) { return (T * k + Tiled::BM - 1) / Tiled::BM + E; }
 int ffn_sq_parts(int64_t H) { return (int)(H / 64); }  // small kernel: 64-column tiles (the finest split)
@@ -512,13 +541,22 @@ hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool buil
                        const_cast<int32_t*>(a.tile_expert), const_cast<int32_t*>(a.tile_row0),
                        const_cast<int32_t*>(a.num_tiles));
   }
+  // the tiles need more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
+  static const hipError_t attr_gu = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, Tiled::kLds);
+  static const hipError_t attr_dn = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, Tiled::kLds);
+  if (attr_gu != hipSuccess) return attr_gu;
+  if (attr_dn != hipSuccess) return attr_dn;
   const unsigned gy = (unsigned)ffn_max_tiles(T, a.k, E);
   if (mode == kGateUp) {
     const unsigned gx = (unsigned)(a.I / Tiled::kHcols);
-    hipLaunchKernelGGL((ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN>), dim3(gx, gy), dim3(256), Tiled::kLds, st, a);
+    hipLaunchKernelGGL((ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>), dim3(gx, gy), dim3(256), Tiled::kLds, st, a);
   } else {
     const unsigned gx = (unsigned)(a.H / Tiled::BN);
-    hipLaunchKernelGGL((ffn_tiled_kernel<kDown, kTiledWM, kTiledWN>), dim3(gx, gy), dim3(256), Tiled::kLds, st, a);
+    hipLaunchKernelGGL((ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>), dim3(gx, gy), dim3(256), Tiled::kLds, st, a);
   }
   return hipGetLastError();
 }

@@ -74,15 +74,26 @@ class Case:
         return dev_bf16(np.stack(self.down), device)
 
 
-def random_case(name, seed, T, H, I, E, k, rsf=2.5, wscale=0.02, xscale=1.0, bias_range=0.1, n_cal=64) -> Case:
+def random_case(name, seed, T, H, I, E, k, rsf=2.5, wscale=0.02, xscale=1.0, bias_range=0.1, n_cal=64,
+                tiny_rows: float = 0.0) -> Case:
+    """A seeded random layer.  tiny_rows > 0 shrinks that fraction of weight rows by
+    2^-10..2^-14 so their E4M3 block scales fall in the subnormal range."""
     rng = np.random.default_rng(seed)
     bf = lambda a: gen.f32_to_bf16_bits(np.asarray(a, np.float32))  # noqa: E731
+
+    def w(shape):
+        a = rng.standard_normal(shape) * wscale
+        if tiny_rows:
+            sel = rng.random(shape[0]) < tiny_rows
+            a[sel] *= np.exp2(-rng.uniform(10, 14, (int(sel.sum()), 1)))
+        return bf(a)
+
     x = bf(rng.standard_normal((T, H)) * xscale)
     wr = bf(rng.standard_normal((E, H)) * 0.02)
     bias = rng.uniform(-bias_range, bias_range, E).astype(np.float32)
-    gate = [bf(rng.standard_normal((I, H)) * wscale) for _ in range(E)]
-    up = [bf(rng.standard_normal((I, H)) * wscale) for _ in range(E)]
-    down = [bf(rng.standard_normal((H, I)) * wscale) for _ in range(E)]
+    gate = [w((I, H)) for _ in range(E)]
+    up = [w((I, H)) for _ in range(E)]
+    down = [w((H, I)) for _ in range(E)]
     f32 = gen.bf16_bits_to_f32
     experts_q = [omoe.quantize_expert(f32(g), f32(u), f32(d)) for g, u, d in zip(gate, up, down)]
     x_cal = bf(rng.standard_normal((n_cal, H)) * xscale)

@@ -228,6 +228,16 @@ def test_layer_parity_random(ops, name, T, H, I, E, k):
     _layer_check(ops, case)
 
 
+@pytest.mark.parametrize("T", [300, 9])  # tiled path, small-M path
+def test_layer_parity_subnormal_weight_scales(ops, T):
+    """A quarter of the weight rows shrunk by 2^-10..2^-14: their E4M3 block
+    scales are subnormal and must decode exactly in the FFN."""
+    case = random_case(f"subnormal_scales_{T}", 31, T, 256, 128, 6, 2, tiny_rows=0.25)
+    subn = sum(int(np.sum(q.gate_scales < 8)) for q in case.experts_q)
+    assert subn > 0
+    _layer_check(ops, case)
+
+
 def test_single_expert_output_is_rsf_times_mlp(ops):
     case = random_case("e1", 11, 24, 256, 128, 1, 1)
     layer, out, ref = _layer_check(ops, case, reap=False)
