@@ -332,6 +332,16 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+  // LDS byte addresses used by the asm fragment reads (see the loop)
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const uint32_t a_lane = (uint32_t)(wm * 32 * WM + r) * 64u;
+  const uint32_t b_lane = (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (uint32_t)(wn * 32 * WN + r) * 64u;
+  const uint32_t as_lane = (uint32_t)S::kACodeBytes + (uint32_t)(wm * 32 * WM + r) * 8u + 4u * g;
+  const uint32_t bs_lane =
+      (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (uint32_t)(wn * 32 * WN + r) * 8u + 4u * g;
+  const uint32_t slot_q0 = (uint32_t)((2 * g) ^ ((r >> 2) & 3)), slot_q1 = (uint32_t)((2 * g + 1) ^ ((r >> 2) & 3));
+  (void)lds_base; (void)a_lane; (void)b_lane; (void)as_lane; (void)bs_lane; (void)slot_q0; (void)slot_q1;
+
   // NS-stage ring: stages st+1 .. st+NS-2 stay in flight while stage st is
   // consumed; one barrier per stage both publishes stage st and frees the
   // buffer of stage st-1 for the next DMA.
@@ -353,38 +363,82 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     asm volatile("" ::: "memory");
     if (st + NS - 1 < nst) issue(st + NS - 1);
     const unsigned char* base = smem + (int)(st % NS) * S::kStage;
-    const uint4* ac = reinterpret_cast<const uint4*>(base);
-    const uint32_t* as = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes);
-    const uint4* bc = reinterpret_cast<const uint4*>(base + S::kACodeBytes + S::kAScaleBytes);
-    const uint32_t* bsc = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes);
+    // this lane's operand words of stage st: code fragments [q][i] (A) and
+    // [q][j] (B), 16 B each, and one scale word per fragment row
+    u32x4_t fa[2][WM], fb[2][WN];
     uint32_t sa[WM], sbv[WN];
+    if constexpr (WM == 4 && WN == 4) {
+      // All reads of the stage in one asm block ending in its own lgkmcnt(0).
+      // Issued by the compiler, an LDS read after the in-flight ring DMA would
+      // get a conservative vmcnt(0) (it cannot tell the ring stages apart),
+      // draining the DMA of the later stages too.  Fragment i of a row block
+      // sits 2048 B (32 rows) after fragment i-1; its scale word 256 B after.
+      const uint32_t sb = lds_base + (uint32_t)(st % NS) * S::kStage;
+      const uint32_t a0 = sb + a_lane + 16u * slot_q0, a1 = sb + a_lane + 16u * slot_q1;
+      const uint32_t b0 = sb + b_lane + 16u * slot_q0, b1 = sb + b_lane + 16u * slot_q1;
+      const uint32_t as_addr = sb + as_lane, bs_addr = sb + bs_lane;
+      asm volatile(
+          "ds_read_b32 %16, %28 offset:0\n"
+          "ds_read_b32 %17, %28 offset:256\n"
+          "ds_read_b32 %18, %28 offset:512\n"
+          "ds_read_b32 %19, %28 offset:768\n"
+          "ds_read_b32 %20, %29 offset:0\n"
+          "ds_read_b32 %21, %29 offset:256\n"
+          "ds_read_b32 %22, %29 offset:512\n"
+          "ds_read_b32 %23, %29 offset:768\n"
+          "ds_read_b128 %0, %24 offset:0\n"
+          "ds_read_b128 %1, %24 offset:2048\n"
+          "ds_read_b128 %2, %24 offset:4096\n"
+          "ds_read_b128 %3, %24 offset:6144\n"
+          "ds_read_b128 %4, %26 offset:0\n"
+          "ds_read_b128 %5, %26 offset:2048\n"
+          "ds_read_b128 %6, %26 offset:4096\n"
+          "ds_read_b128 %7, %26 offset:6144\n"
+          "ds_read_b128 %8, %25 offset:0\n"
+          "ds_read_b128 %9, %25 offset:2048\n"
+          "ds_read_b128 %10, %25 offset:4096\n"
+          "ds_read_b128 %11, %25 offset:6144\n"
+          "ds_read_b128 %12, %27 offset:0\n"
+          "ds_read_b128 %13, %27 offset:2048\n"
+          "ds_read_b128 %14, %27 offset:4096\n"
+          "ds_read_b128 %15, %27 offset:6144\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[0][2]), "=&v"(fa[0][3]), "=&v"(fb[0][0]),
+            "=&v"(fb[0][1]), "=&v"(fb[0][2]), "=&v"(fb[0][3]), "=&v"(fa[1][0]), "=&v"(fa[1][1]),
+            "=&v"(fa[1][2]), "=&v"(fa[1][3]), "=&v"(fb[1][0]), "=&v"(fb[1][1]), "=&v"(fb[1][2]),
+            "=&v"(fb[1][3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sbv[0]),
+            "=&v"(sbv[1]), "=&v"(sbv[2]), "=&v"(sbv[3])
+          : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(as_addr), "v"(bs_addr)
+          : "memory");
+    } else {
+      const uint32_t* as = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes);
+      const uint32_t* bsc = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes);
+      const u32x4_t* ac = reinterpret_cast<const u32x4_t*>(base);
+      const u32x4_t* bc = reinterpret_cast<const u32x4_t*>(base + S::kACodeBytes + S::kAScaleBytes);
 #pragma unroll
-    for (int i = 0; i < WM; ++i) sa[i] = as[(wm * 32 * WM + 32 * i + r) * 2 + g];
+      for (int i = 0; i < WM; ++i) sa[i] = as[(wm * 32 * WM + 32 * i + r) * 2 + g];
 #pragma unroll
-    for (int j = 0; j < WN; ++j) sbv[j] = bsc[(wn * 32 * WN + 32 * j + r) * 2 + g];
+      for (int j = 0; j < WN; ++j) sbv[j] = bsc[(wn * 32 * WN + 32 * j + r) * 2 + g];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        // rows below are r + multiples of 32, so (row >> 2) & 3 == (r >> 2) & 3
+        const int slot = (2 * g + q) ^ ((r >> 2) & 3);
+#pragma unroll
+        for (int i = 0; i < WM; ++i) fa[q][i] = ac[(wm * 32 * WM + 32 * i + r) * 4 + slot];
+#pragma unroll
+        for (int j = 0; j < WN; ++j) fb[q][j] = bc[(wn * 32 * WN + 32 * j + r) * 4 + slot];
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      uint4 ca[WM], cbq[WN];
-      // rows below are r + multiples of 32, so (row >> 2) & 3 == (r >> 2) & 3
-      const int slot = (2 * g + q) ^ ((r >> 2) & 3);
-#pragma unroll
-      for (int i = 0; i < WM; ++i) ca[i] = ac[(wm * 32 * WM + 32 * i + r) * 4 + slot];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) cbq[j] = bc[(wn * 32 * WN + 32 * j + r) * 4 + slot];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int sbyte = 2 * q + (s >> 1);
         half8_t af[WM], bf[WN];
 #pragma unroll
-        for (int i = 0; i < WM; ++i) {
-          const uint32_t w = s == 0 ? ca[i].x : s == 1 ? ca[i].y : s == 2 ? ca[i].z : ca[i].w;
-          af[i] = decode8(w, scale_pair(sa[i], sbyte));
-        }
+        for (int i = 0; i < WM; ++i) af[i] = decode8(fa[q][i][s], scale_pair(sa[i], sbyte));
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const uint32_t w = s == 0 ? cbq[j].x : s == 1 ? cbq[j].y : s == 2 ? cbq[j].z : cbq[j].w;
-          bf[j] = decode8(w, scale_pair(sbv[j], sbyte));
-        }
+        for (int j = 0; j < WN; ++j) bf[j] = decode8(fb[q][j][s], scale_pair(sbv[j], sbyte));
 #pragma unroll
         for (int i = 0; i < WM; ++i)
 #pragma unroll
