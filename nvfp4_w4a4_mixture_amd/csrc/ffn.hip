@@ -53,6 +53,18 @@ struct SmallIter {
   uint32_t bs[4];
 };
 
+#ifndef MOE_SMALL_NT
+#define MOE_SMALL_NT 0  // plain loads measured faster than non-temporal ones for this stream
+#endif
+// the decode kernel's weight stream: each byte is read once
+__device__ __forceinline__ u32x4_t load_stream(const u32x4_t* p) {
+#if MOE_SMALL_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 template <int KB>
 __device__ __forceinline__ uint32_t load_scales(const uint8_t* p) {
   if (KB == 256) return *reinterpret_cast<const uint32_t*>(p);
@@ -105,7 +117,7 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int q = 0; q < kDw / 4; ++q)
-        d.bc[j][q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(b_code_row[j] + cb + 16 * q));
+        d.bc[j][q] = load_stream(reinterpret_cast<const u32x4_t*>(b_code_row[j] + cb + 16 * q));
       d.bs[j] = load_scales<KB>(b_scale_row[j] + sb);
     }
   };

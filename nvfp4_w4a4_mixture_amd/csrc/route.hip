@@ -8,13 +8,18 @@
 // route_logits_kernel: FP64 logit partials for a 64-token tile over one range
 // of the hidden dimension, from BF16 x and W_r staged through LDS (every
 // product and sum is FP64).  route_select_kernel: one wave per token sums the
-// partials in a fixed order and selects the top-k with wave-wide argmax
-// reductions.  Selection decides integers, so it runs in FP64 like the
-// definition it follows; ties go to the lower expert index.
+// partials in a fixed order and ranks every expert under (score descending,
+// expert ascending); rank < k is slot `rank` of the top-k.  Selection decides
+// integers, so it runs in FP64 like the definition it follows; ties go to the
+// lower expert index.
 //
 // The permutation is a stable counting sort in three passes over chunks of
 // kPermChunk pairs: per-chunk histograms, a per-expert scan over chunks, and a
 // per-chunk scatter that ranks equal experts by pair id with wave ballots.
+//
+// Decode batches (T <= 16) take two kernels instead: logits over 256-wide
+// hidden slices with the router weights in registers, then selection and the
+// whole counting sort in one workgroup.
 #include "device_common.h"
 #include "launch.h"
 
@@ -104,77 +109,282 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
   }
 }
 
-// One wave per token: logit = sum of the partials in split order; score =
-// sigmoid(logit) + bias; k rounds of a wave-wide argmax under the total order
-// (score descending, expert ascending); weights rsf * s_j / sum s.
+// Orders this wave's LDS writes before its later LDS reads (lanes read what
+// other lanes of the same wave wrote).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// z[i] = sum over splits s (in order) of pt[s * stride + ec[i]], i < NG.
+// Top-k of one token by one wave from its scores.  Lane holds, for the
+// experts e = lane + 64 i (i < NG, e < E), sg = sigmoid(logit) and
+// sc = sg + bias.  The top-k are the experts whose rank under the total order
+// (score descending, expert ascending) is below k: each lane ranks its experts
+// against every score, broadcast from the wave's LDS row `row` (>= E + 1
+// doubles, 16-byte aligned; padded to an even length with -inf, which
+// outranks nothing), so slot j holds the j-th expert of that order.  The row
+// is then reused for the selected sg; weights are rsf * s_j / sum s, the sum
+// taken over j = 0..k-1 in order.  On return slot[i] = 1 + the slot of expert
+// lane + 64 i (0: not chosen).
+template <int NG>
+__device__ __forceinline__ void rank_select(const double (&sg)[NG], const double (&sc)[NG], int64_t t, int E, int k,
+                                            float rsf, int lane, double* row, int32_t* __restrict__ topk_ids,
+                                            float* __restrict__ topk_w, int (&slot)[4]) {
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+    if (lane + 64 * i < E) row[lane + 64 * i] = sc[i];
+  if (lane == 0 && (E & 1)) row[E] = -__builtin_inf();
+  wave_lds_sync();
+  int rank[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) rank[i] = 0;
+  const int npair = (E + 1) >> 1;
+#pragma unroll 4
+  for (int q = 0; q < npair; ++q) {
+    const double2 v = reinterpret_cast<const double2*>(row)[q];
+    const int e0 = 2 * q;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int e = lane + 64 * i;
+      rank[i] += (int)(v.x > sc[i]) | ((int)(v.x == sc[i]) & (int)(e0 < e));
+      rank[i] += (int)(v.y > sc[i]) | ((int)(v.y == sc[i]) & (int)(e0 + 1 < e));
+    }
+  }
+  wave_lds_sync();  // every lane has read the scores; the row now takes sg by slot
+#pragma unroll
+  for (int i = 0; i < 4; ++i) slot[i] = 0;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E && rank[i] < k) {
+      slot[i] = rank[i] + 1;
+      topk_ids[t * k + rank[i]] = e;
+      row[rank[i]] = sg[i];
+    }
+  }
+  wave_lds_sync();
+  double ssum = 0.0;
+  for (int j = 0; j < k; ++j) ssum += row[j];
+  for (int j = lane; j < k; j += 64) topk_w[t * k + j] = (float)((double)rsf * row[j] / ssum);
+  wave_lds_sync();  // the row is reused by the wave's next token
+}
+
+// General path: one wave per token sums the partials in split order (lanes
+// past E read expert E-1 and ignore it, so every load is unconditional and
+// the loads of several splits are in flight together), then rank_select.
+template <int NG>
+__device__ __forceinline__ void select_token_ng(const double* __restrict__ part, int64_t nsplit, int64_t T, int64_t t,
+                                                const float* __restrict__ bias, int E, int k, float rsf, int lane,
+                                                double* row, int32_t* __restrict__ topk_ids,
+                                                float* __restrict__ topk_w, int (&slot)[4]) {
+  int ec[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) ec[i] = lane + 64 * i < E ? lane + 64 * i : E - 1;
+  double z[NG], b[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    z[i] = 0.0;
+    b[i] = (double)bias[ec[i]];
+  }
+  const double* pt = part + t * E;
+  const int64_t stride = T * E;
+#pragma unroll 8
+  for (int64_t s = 0; s < nsplit; ++s) {  // fixed order over splits
+    const double* ps = pt + s * stride;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) z[i] += ps[ec[i]];
+  }
+  double sg[NG], sc[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    sg[i] = 1.0 / (1.0 + exp(-z[i]));
+    sc[i] = sg[i] + b[i];
+  }
+  rank_select<NG>(sg, sc, t, E, k, rsf, lane, row, topk_ids, topk_w, slot);
+}
+
 __global__ __launch_bounds__(256) void route_select_kernel(const double* __restrict__ part, int64_t nsplit, int64_t T,
                                                            const float* __restrict__ bias, int E, int k, float rsf,
                                                            int32_t* __restrict__ topk_ids,
                                                            float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ __align__(16) double rows[4][258];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= T) return;
-  double sc[4], sg[4];
-  bool taken[4];
+  int slot[4];
+  double* row = rows[wave];
+  switch ((E + 63) >> 6) {
+    case 1: select_token_ng<1>(part, nsplit, T, t, bias, E, k, rsf, lane, row, topk_ids, topk_w, slot); break;
+    case 2: select_token_ng<2>(part, nsplit, T, t, bias, E, k, rsf, lane, row, topk_ids, topk_w, slot); break;
+    case 3: select_token_ng<3>(part, nsplit, T, t, bias, E, k, rsf, lane, row, topk_ids, topk_w, slot); break;
+    default: select_token_ng<4>(part, nsplit, T, t, bias, E, k, rsf, lane, row, topk_ids, topk_w, slot); break;
+  }
+}
+
+// Decode batches (T <= kDecT).  Logits: each workgroup takes kDecH hidden
+// elements for up to 64 experts; wave w takes the w-th quarter of that range,
+// lane = expert, with the lane's 64 router weights in registers and the tokens'
+// x values broadcast from LDS.  Quarter sums are added in wave order, so the
+// partial for (split, t, e) is one fixed sum.  Requires 16-byte aligned x and
+// W_r rows (ldx % 8 == 0, H % 8 == 0).
+constexpr int kDecT = 16, kDecH = 256;
+static inline int64_t dec_nsplit(int64_t H) { return (H + kDecH - 1) / kDecH; }
+
+__global__ __launch_bounds__(256) void route_logits_decode_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t H,
+                                                                  int64_t ldx, const uint16_t* __restrict__ wr,
+                                                                  int E, double* __restrict__ part) {
+  __shared__ __align__(16) double xs[kDecH][kDecT];
+  __shared__ double red[3][kDecT][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t split = blockIdx.x;
+  const int64_t h0 = split * kDecH;
+  const int e = blockIdx.y * 64 + lane;
+  // this lane's 64 router weights: row e, columns h0 + 64*wave ...
+  u32x4_t wv[8];
+  const int64_t hw = h0 + 64 * wave;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    taken[i] = (e >= E);
-    sg[i] = 0.0;
-    sc[i] = 0.0;
-    if (e < E) {
-      double z = 0.0;
-#pragma unroll 8
-      for (int64_t s = 0; s < nsplit; ++s) z += part[(s * T + t) * E + e];  // fixed order
-      sg[i] = 1.0 / (1.0 + exp(-z));
-      sc[i] = sg[i] + (double)bias[e];
+  for (int c = 0; c < 8; ++c) {
+    const int64_t h = hw + 8 * c;
+    wv[c] = (e < E && h < H) ? *reinterpret_cast<const u32x4_t*>(wr + (int64_t)e * H + h) : u32x4_t{0, 0, 0, 0};
+  }
+  // stage x[t][h0 .. h0+256) as FP64, transposed to xs[h][t]; zero past T and H
+  {
+    const int t = tid & 15, c0 = (tid >> 4) * 16;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int c = c0 + 8 * half;
+      const int64_t h = h0 + c;
+      u32x4_t v = {0, 0, 0, 0};
+      if (t < T && h < H) v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)t * ldx + h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xs[c + 2 * q][t] = (double)__uint_as_float(v[q] << 16);
+        xs[c + 2 * q + 1][t] = (double)__uint_as_float(v[q] & 0xFFFF0000u);
+      }
     }
   }
-  double ssum = 0.0;
-  int my_e[4] = {0, 0, 0, 0};  // slot j is kept by lane j % 64 in my_e[j / 64]
-  double my_s[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int j = 0; j < k; ++j) {
-    double bs = -__builtin_inf();
-    int be = 0x7FFFFFFF;
-    double bg = 0.0;
+  __syncthreads();
+  double acc[kDecT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!taken[i] && (sc[i] > bs || be == 0x7FFFFFFF)) {  // i ascending = expert ascending
-        bs = sc[i];
-        be = lane + 64 * i;
-        bg = sg[i];
-      }
+  for (int t = 0; t < kDecT; ++t) acc[t] = 0.0;
+#pragma unroll 2
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t word = wv[c][q >> 1];
+      const double w = (double)__uint_as_float((q & 1) ? (word & 0xFFFF0000u) : (word << 16));
+      const double* xr = xs[64 * wave + 8 * c + q];
+#pragma unroll
+      for (int t = 0; t < kDecT; ++t) acc[t] = __builtin_fma(xr[t], w, acc[t]);
     }
+  }
+  if (wave > 0) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const double os = __shfl_xor(bs, off);
-      const int oe = __shfl_xor(be, off);
-      const double og = __shfl_xor(bg, off);
-      if (os > bs || (os == bs && oe < be)) {
-        bs = os;
-        be = oe;
-        bg = og;
+    for (int t = 0; t < kDecT; ++t) red[wave - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (wave == 0 && e < E) {
+    for (int t = 0; t < T; ++t) {
+      const double z = ((acc[t] + red[0][t][lane]) + red[1][t][lane]) + red[2][t][lane];
+      part[(split * T + t) * E + e] = z;
+    }
+  }
+}
+
+// Decode batches: logits, selection and the whole stable counting sort in one
+// workgroup of 16 waves.  First every thread reduces (token, expert) partial
+// sums in split order with the loads of up to 32 splits in flight, into an
+// LDS row per token; then wave t selects for token t from its row.
+// slot[t][e] = 1 + the top-k slot in which token t chose expert e (0: not
+// chosen); a pair's rank inside its expert is the number of earlier tokens
+// that chose the same expert, which is the order of pair ids.
+template <int NG>
+__device__ __forceinline__ void select_decode_token(double* row, const float* bias_l, int64_t t, int E, int k,
+                                                    float rsf, int lane, int32_t* __restrict__ topk_ids,
+                                                    float* __restrict__ topk_w, int (&slot)[4]) {
+  double sg[NG], sc[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int e = lane + 64 * i < E ? lane + 64 * i : E - 1;
+    sg[i] = 1.0 / (1.0 + exp(-row[e]));
+    sc[i] = sg[i] + (double)bias_l[e];
+  }
+  wave_lds_sync();  // logits read before rank_select overwrites the row
+  rank_select<NG>(sg, sc, t, E, k, rsf, lane, row, topk_ids, topk_w, slot);
+}
+
+__global__ __launch_bounds__(1024) void route_select_permute_decode_kernel(
+    const double* __restrict__ part, int64_t nsplit, int64_t T, const float* __restrict__ bias, int E, int k,
+    float rsf, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
+  constexpr int kBatch = 32;
+  __shared__ __align__(16) double rows[kDecT][258];
+  __shared__ float bias_l[256];
+  __shared__ uint16_t slot[kDecT][256];
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kDecT * 256; i += 1024) (&slot[0][0])[i] = 0;
+  if (tid < E) bias_l[tid] = bias[tid];
+  const int64_t npe = T * E;
+  for (int64_t p = tid; p < npe; p += 1024) {
+    const double* pp = part + p;  // part[(s * T + t) * E + e] = pp[s * T * E] with p = t * E + e
+    double z = 0.0;
+    for (int64_t s0 = 0; s0 < nsplit; s0 += kBatch) {
+      double v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int64_t sj = s0 + j < nsplit ? s0 + j : nsplit - 1;
+        v[j] = pp[sj * npe];
       }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (s0 + j < nsplit) z += v[j];
+    }
+    const int64_t t = p / E;
+    rows[t][p - t * E] = z;
+  }
+  __syncthreads();
+  if (wave < T) {
+    int sl[4];
+    const int64_t t = wave;
+    switch ((E + 63) >> 6) {
+      case 1: select_decode_token<1>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
+      case 2: select_decode_token<2>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
+      case 3: select_decode_token<3>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
+      default: select_decode_token<4>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == be) taken[i] = true;
-    ssum += bg;  // every lane sums in the same order j = 0..k-1
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (i == (j >> 6) && lane == (j & 63)) {
-        my_e[i] = be;
-        my_s[i] = bg;
-      }
+      if (lane + 64 * i < E) slot[t][lane + 64 * i] = (uint16_t)sl[i];
   }
+  __syncthreads();
+  // per-expert counts and an exclusive scan over experts (threads 0..255)
+  int cnt = 0;
+  if (tid < E)
+    for (int t = 0; t < T; ++t) cnt += (slot[t][tid] != 0);
+  int incl = cnt;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = lane + 64 * i;
-    if (j < k) {
-      topk_ids[t * k + j] = my_e[i];
-      topk_w[t * k + j] = (float)((double)rsf * my_s[i] / ssum);
+  for (int off = 1; off < 64; off <<= 1) {
+    const int n = __shfl_up(incl, off);
+    if (lane >= off) incl += n;
+  }
+  if (lane == 63 && wave < 4) wsum[wave] = incl;
+  __syncthreads();
+  int pre = 0;
+  for (int w = 0; w < wave && w < 4; ++w) pre += wsum[w];
+  const int base = pre + incl - cnt;
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = base;
+    int r = base;
+    for (int t = 0; t < T; ++t) {
+      const int sl = slot[t][tid];
+      if (sl) sorted[r++] = (int32_t)(t * k + sl - 1);
     }
   }
+  if (tid == 0) offsets[E] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
 // Per-chunk expert histograms: counts[c][e] for chunk c of kPermChunk pairs.
@@ -275,7 +485,9 @@ size_t route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k) {
   const int64_t npairs = T * k;
   const int64_t nchunks = (npairs + kPermChunk - 1) / kPermChunk;
   const RouteSplit sp = route_split(T, H);
-  return align256((size_t)(2 * nchunks * E * 4)) + (size_t)(sp.nsplit * T * E * 8);
+  int64_t nsplit = sp.nsplit;
+  if (T <= kDecT && dec_nsplit(H) > nsplit) nsplit = dec_nsplit(H);
+  return align256((size_t)(2 * nchunks * E * 4)) + (size_t)(nsplit * T * E * 8);
 }
 
 template <int JE>
@@ -297,9 +509,18 @@ hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, co
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, st, chunk_counts, 0, e, chunk_base, counts, offsets);
     return hipGetLastError();
   }
-  const RouteSplit sp = route_split(T, H);
   double* part = reinterpret_cast<double*>(static_cast<unsigned char*>(workspace) +
                                            align256((size_t)(2 * nchunks * E * 4)));
+  const bool vec16 = (H % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)wr % 16 == 0);
+  if (T <= kDecT && vec16) {
+    const int64_t ns = dec_nsplit(H);
+    hipLaunchKernelGGL(route_logits_decode_kernel, dim3((unsigned)ns, (unsigned)((e + 63) / 64)), dim3(256), 0, st,
+                       x, T, H, ldx, wr, e, part);
+    hipLaunchKernelGGL(route_select_permute_decode_kernel, dim3(1), dim3(1024), 0, st, part, ns, T, bias, e, kk, rsf,
+                       topk_ids, topk_w, counts, offsets, sorted);
+    return hipGetLastError();
+  }
+  const RouteSplit sp = route_split(T, H);
   switch ((e + 15) / 16) {
 #define LG(N) \
   case N: launch_logits<N>(x, T, H, ldx, wr, e, sp, part, st); break;

@@ -119,8 +119,11 @@ def test_quantize_weights_bitexact(ops):
 # ---------------------------------------------------------------------------
 # routing + permutation
 
+# T <= 16 with 16-byte aligned rows takes the decode kernels (H-sliced logits, one-workgroup select+permute);
+# larger batches the tiled logits and the chunked counting sort
 @pytest.mark.parametrize("T,H,E,k", [(64, 256, 8, 2), (300, 512, 80, 8), (1000, 256, 128, 8), (37, 64, 256, 16),
-                                     (5, 32, 1, 1), (3, 32, 16, 16), (2500, 128, 80, 8), (0, 64, 8, 2)])
+                                     (5, 32, 1, 1), (3, 32, 16, 16), (2500, 128, 80, 8), (0, 64, 8, 2),
+                                     (64, 64, 128, 16), (16, 6144, 80, 8), (16, 6144, 256, 256), (13, 520, 200, 9)])
 def test_route_and_permutation_bitexact(ops, T, H, E, k):
     say(f"route T={T} H={H} E={E} k={k}")
     rng = np.random.default_rng(T * 31 + E)
@@ -144,8 +147,32 @@ def test_route_and_permutation_bitexact(ops, T, H, E, k):
     assert np.array_equal(perm, p_ref)
 
 
-def test_route_exact_ties_go_to_lower_index(ops):
-    say("route crafted ties")
+@pytest.mark.parametrize("T,H,pad", [(10, 256, 4), (10, 256, 8), (16, 1024, 24)])
+def test_route_strided_rows(ops, T, H, pad):
+    """x as a column slice of a wider buffer: ldx % 8 != 0 takes the general path at decode sizes."""
+    say(f"route strided T={T} H={H} ldx={H + pad}")
+    E, k, rsf = 40, 6, 1.5
+    rng = np.random.default_rng(T + pad)
+    xw = gen.f32_to_bf16_bits(rng.standard_normal((T, H + pad)).astype(np.float32))
+    wr = gen.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    x = dev_bf16(xw)[:, :H]
+    assert x.stride(0) == H + pad
+    out = ops.moe_route(x, dev_bf16(wr), torch.from_numpy(bias).cuda(), k, rsf)
+    torch.cuda.synchronize()
+    xb = np.ascontiguousarray(xw[:, :H])
+    ref = dict(zip(("ids", "weights", "weights64", "gap"), oroute.route(xb, wr, bias, k, rsf)))
+    ids = to_np(out.topk_ids)
+    assert check_routing(ids, to_np(out.topk_w), ref, rsf, E) == 0
+    c_ref, o_ref, p_ref = oracle_perm(ids, E)
+    assert np.array_equal(to_np(out.expert_counts), c_ref)
+    assert np.array_equal(to_np(out.expert_offsets), o_ref)
+    assert np.array_equal(to_np(out.sorted_pair_ids), p_ref)
+
+
+@pytest.mark.parametrize("T", [12, 40, 200])  # decode path, general path (one and several chunks)
+def test_route_exact_ties_go_to_lower_index(ops, T):
+    say(f"route crafted ties T={T}")
     H, E, k = 64, 12, 4
     rng = np.random.default_rng(8)
     wr = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
@@ -155,7 +182,7 @@ def test_route_exact_ties_go_to_lower_index(ops):
     wrb = gen.f32_to_bf16_bits(wr)
     bias = np.zeros(E, np.float32)
     bias[2] = bias[5] = bias[9] = 2.0  # score > 2 > any other: tied experts 2, 5, 9 lead every token
-    xb = gen.f32_to_bf16_bits(rng.standard_normal((40, H)).astype(np.float32))
+    xb = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     out = ops.moe_route(dev_bf16(xb), dev_bf16(wrb), torch.from_numpy(bias).cuda(), k, 1.0)
     ids = to_np(out.topk_ids)
     ref_ids, _, _, _ = oroute.route(xb, wrb, bias, k, 1.0)
