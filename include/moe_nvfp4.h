@@ -35,10 +35,18 @@
  *             saturating at 448; a zero S gives 16 zero codes; otherwise
  *             code = E2M1 RNE-even(f32(x * f32(gs / S))), saturating at 6,
  *             sign bit = sign bit of that product.
- *  Weights    w13 codes [E, 2I, H/2], scales [E, 2I, H/16], gs [E, 2]:
- *             rows 0..I-1 of an expert are the gate projection, rows I..2I-1
- *             the up projection, each with its own global scale.
- *             w2 codes [E, H, I/2], scales [E, H, I/16], gs [E].
+ *  Weights    w13 codes [E, 2I, H/2], scales tiled over the 2I*E rows,
+ *             gs [E, 2]: rows 0..I-1 of an expert are the gate projection,
+ *             rows I..2I-1 the up projection, each with its own global scale.
+ *             w2 codes [E, H, I/2], scales tiled over the E*H rows, gs [E].
+ *             Tiled scales (weights only): the same bytes as a row-major
+ *             [R, K/16] array (R rows, K columns, R % 16 == 0, K % 128 == 0),
+ *             reordered so that the 8 scales of 16 consecutive rows r and
+ *             128 consecutive columns form one 128-byte block:
+ *               byte of (row r, block b = column / 16) =
+ *                 (r / 16) * K + (b / 8) * 128 + (r % 16) * 8 + b % 8,
+ *             i.e. an array [R/16, K/128, 16, 8].  A K-step of an expert
+ *             kernel then reads its 16 rows' scales as one contiguous run.
  *  Errors     Arguments are validated on the host before anything is
  *             enqueued.  A failed check returns its status, enqueues nothing
  *             and writes no output.  T == 0 (rows == 0) is a successful no-op
@@ -61,7 +69,7 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 1
+#define MOE_NVFP4_ABI_VERSION 2
 
 typedef int32_t moe_status;
 #define MOE_OK 0
@@ -122,10 +130,11 @@ moe_status nvfp4_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols
 /* Offline round-to-nearest quantization of `batch` BF16 weight matrices
  * [batch, rows, cols] (contiguous), each with its own global scale
  * gs[b] = f32(2688 / amax(|W_b|)) (1 when W_b is all zero), written to
- * global_scales [batch].  codes [batch, rows, cols/2], scales
- * [batch, rows, cols/16].  For w13 pass batch = 2E, rows = I (gate and up
- * are separate Linear modules, "per-expert Linear granularity"); for w2 pass
- * batch = E, rows = H.  cols % 16 == 0; w_bf16 16-byte aligned. */
+ * global_scales [batch].  codes [batch, rows, cols/2]; scales tiled over the
+ * batch*rows rows (layout in the header comment, K = cols).  For w13 pass
+ * batch = 2E, rows = I (gate and up are separate Linear modules,
+ * "per-expert Linear granularity"); for w2 pass batch = E, rows = H.
+ * rows % 16 == 0, cols % 128 == 0; w_bf16 16-byte aligned. */
 moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t rows, int64_t cols,
                                   uint8_t* codes, uint8_t* scales_e4m3, float* global_scales,
                                   void* stream);

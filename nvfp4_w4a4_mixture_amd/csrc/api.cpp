@@ -140,15 +140,16 @@ moe_status nvfp4_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols
   if (ld % 8 != 0 || !aligned(x_bf16, 16) || !aligned(codes, 8))
     return fail(MOE_ERR_ALIGN, "nvfp4_quantize_act: x must be 16-byte aligned with ld %% 8 == 0; codes 8-byte aligned");
   if (moe_status s = check_device()) return s;
-  return launched(moe::launch_quantize_bf16(x_bf16, rows, cols, ld, global_scale, rows, codes, scales_e4m3,
+  return launched(moe::launch_quantize_bf16(x_bf16, rows, cols, ld, global_scale, rows, codes, scales_e4m3, false,
                                             (hipStream_t)stream),
                   "nvfp4_quantize_act");
 }
 
 moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
                                   uint8_t* scales_e4m3, float* global_scales, void* stream) {
-  if (batch < 0 || rows <= 0 || cols <= 0 || cols % 16 != 0)
-    return fail(MOE_ERR_SHAPE, "nvfp4_quantize_weights: need batch >= 0, rows > 0, cols a positive multiple of 16");
+  if (batch < 0 || rows <= 0 || rows % 16 != 0 || cols <= 0 || cols % 128 != 0)
+    return fail(MOE_ERR_SHAPE,
+                "nvfp4_quantize_weights: need batch >= 0, rows a positive multiple of 16, cols a positive multiple of 128");
   if (batch == 0) return MOE_OK;
   if (!w_bf16 || !codes || !scales_e4m3 || !global_scales)
     return fail(MOE_ERR_NULL, "nvfp4_quantize_weights: a required pointer is NULL");
@@ -160,7 +161,7 @@ moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t
                               "nvfp4_quantize_weights (global scales)"))
     return s;
   return launched(moe::launch_quantize_bf16(w_bf16, batch * rows, cols, cols, global_scales, rows, codes, scales_e4m3,
-                                            st),
+                                            true, st),
                   "nvfp4_quantize_weights");
 }
 

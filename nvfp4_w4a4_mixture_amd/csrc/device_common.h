@@ -114,4 +114,12 @@ __device__ __forceinline__ half2_t scale_pair(uint32_t scales4, int k) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Weight block scales are stored tiled: the 16 x 8 scale bytes of 16
+// consecutive rows and 128 consecutive columns form one 128-byte block
+// (row-major inside), blocks ordered by column within a 16-row tile and tiles
+// by row.  Byte of (row, scale block b = column / 16) for K columns:
+__host__ __device__ __forceinline__ int64_t tiled_scale_index(int64_t row, int64_t b, int64_t K) {
+  return (row >> 4) * K + (b >> 3) * 128 + (row & 15) * 8 + (b & 7);
+}
+
 }  // namespace moe

@@ -19,9 +19,9 @@
 //
 // Two kernels:
 //  * ffn_small_kernel (decode batches, every expert has <= 16 pairs): one
-//    workgroup per (expert, 64-row weight tile); each of the four waves takes
-//    a contiguous quarter of K in 256-element iterations (a full 128-byte line
-//    per weight row), prefetching the next iteration into registers; weights
+//    workgroup per (expert, 64-row weight tile); the four waves take
+//    256-element K iterations in turn (a full 128-byte line per weight row),
+//    each prefetching its next iteration into registers; weights
 //    go straight from HBM to registers (each weight byte is used once),
 //    16x16x32 MFMA; the waves' partial sums meet in LDS.
 //  * ffn_tiled_kernel (any M): one workgroup per (m-tile of an expert's
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
       brow = (int64_t)e * a.H + (int64_t)tile * 64 + 16 * j + c;
     }
     b_code_row[j] = a.b_codes + brow * kbytes + g * (KB / 8);
-    b_scale_row[j] = a.b_scales + brow * kscales + g * (KB / 64);
+    // tiled scales: a K iteration of 16 rows is KB contiguous bytes (KB / 128 blocks)
+    b_scale_row[j] = a.b_scales + tiled_scale_index(brow, 0, K) + (KB == 256 ? (g >> 1) * 128 + 4 * (g & 1) : 2 * g);
   }
 
   auto load = [&](int64_t it, It& d) {
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
 #pragma unroll
       for (int q = 0; q < kDw / 4; ++q)
         d.bc[j][q] = load_stream(reinterpret_cast<const u32x4_t*>(b_code_row[j] + cb + 16 * q));
-      d.bs[j] = load_scales<KB>(b_scale_row[j] + sb);
+      d.bs[j] = load_scales<KB>(b_scale_row[j] + it * KB);
     }
   };
 
@@ -138,15 +139,15 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
     }
   };
 
-  // each wave takes a contiguous range of K iterations; the next iteration's
-  // loads are in flight while the current one is decoded and multiplied
+  // wave w takes K iterations w, w + 4, ...: at any time the four waves read
+  // neighbouring lines of each weight row; the next iteration's loads are in
+  // flight while the current one is decoded and multiplied
   const int64_t nit = K / KB;
-  const int64_t it0 = (wave * nit) / 4, it1 = ((wave + 1) * nit) / 4;
-  if (it0 < it1) {
+  if (wave < nit) {
     It cur, nxt;
-    load(it0, cur);
-    for (int64_t it = it0; it < it1; ++it) {
-      if (it + 1 < it1) load(it + 1, nxt);
+    load(wave, cur);
+    for (int64_t it = wave; it < nit; it += 4) {
+      if (it + 4 < nit) load(it + 4, nxt);
       compute(cur);
       cur = nxt;
     }
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 #pragma unroll
   for (int i = 0; i < S::kBScaleOps; ++i) {
     const int row = 32 * (4 * i + wave) + (lane >> 1);
-    b_scale_src[i] = a.b_scales + b_row(row) * kscales + 4 * (lane & 1);
+    b_scale_src[i] = a.b_scales + tiled_scale_index(b_row(row), 0, K) + 4 * (lane & 1);  // tiled: 128 B per stage
   }
 
   auto issue = [&](int64_t st) {
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
       dma16(b_code_src[i] + cbo, base + S::kACodeBytes + S::kAScaleBytes + (4 * i + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < S::kBScaleOps; ++i)
-      dma4(b_scale_src[i] + sbo, base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes + (4 * i + wave) * 256);
+      dma4(b_scale_src[i] + st * 128, base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes + (4 * i + wave) * 256);
   };
 
   float16_t acc[WM][WN];

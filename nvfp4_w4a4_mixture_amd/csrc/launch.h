@@ -35,7 +35,8 @@ struct FfnArgs {
 };
 
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* gs,
-                                int64_t rows_per_gs, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                                int64_t rows_per_gs, uint8_t* codes, uint8_t* scales, bool tiled_scales,
+                                hipStream_t stream);
 hipError_t launch_weight_global_scales(const uint16_t* w, int64_t batch, int64_t per_matrix, float* gs,
                                        hipStream_t stream);
 

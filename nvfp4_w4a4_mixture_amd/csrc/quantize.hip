@@ -4,7 +4,10 @@
 // weights round-to-nearest per expert Linear).
 //
 // One thread quantizes one 16-element block: it reads 32 contiguous bytes of
-// BF16, writes 8 bytes of codes and 1 scale byte.  Consecutive threads take
+// BF16, writes 8 bytes of codes and 1 scale byte.  Activation scales are
+// row-major [rows, cols/16]; weight scales go to the tiled layout the expert
+// kernels read (16 rows x 128 columns = one 128-byte block, see
+// tiled_scale_index).  Consecutive threads take
 // consecutive blocks of a row, so a wave reads 2 KiB and writes 512 B + 64 B
 // contiguously: the kernel streams HBM at its roofline (2.5625 B/element).
 #include "device_common.h"
@@ -15,7 +18,8 @@ namespace moe {
 __global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __restrict__ x, int64_t rows,
                                                             int64_t blocks_per_row, int64_t ld,
                                                             const float* __restrict__ gs, int64_t rows_per_gs,
-                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                            int tiled) {
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= rows * blocks_per_row) return;
   const int64_t r = b / blocks_per_row;
@@ -34,7 +38,7 @@ __global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __re
   uint32_t lo, hi;
   const uint32_t sc = quantize_block16(f, g, lo, hi);
   reinterpret_cast<uint2*>(codes)[b] = make_uint2(lo, hi);
-  scales[b] = (uint8_t)sc;
+  scales[tiled ? tiled_scale_index(r, c, blocks_per_row * 16) : b] = (uint8_t)sc;
 }
 
 // amax per matrix of a [batch, per_matrix] BF16 array, as float bits
@@ -78,13 +82,14 @@ __global__ void global_scale_kernel(float* gs, int64_t n) {
 }
 
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* gs,
-                                int64_t rows_per_gs, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                                int64_t rows_per_gs, uint8_t* codes, uint8_t* scales, bool tiled_scales,
+                                hipStream_t stream) {
   const int64_t bpr = cols / 16;
   const int64_t n = rows * bpr;
   if (n == 0) return hipSuccess;
   const int64_t grid = (n + 255) / 256;
   hipLaunchKernelGGL(quantize_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, rows, bpr, ld, gs,
-                     rows_per_gs, codes, scales);
+                     rows_per_gs, codes, scales, tiled_scales ? 1 : 0);
   return hipGetLastError();
 }
 

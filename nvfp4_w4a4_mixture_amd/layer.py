@@ -53,8 +53,8 @@ class NVFP4MoELayer:
         I = two_i // 2
         c13, s13, g13 = ops.nvfp4_quantize_weights(w13_bf16.view(2 * E, I, H))
         c2, s2, g2 = ops.nvfp4_quantize_weights(w2_bf16)
-        return cls(w_router_bf16, bias, k, rsf, x_gs, h_gs, c13.view(E, 2 * I, H // 2), s13.view(E, 2 * I, H // 16),
-                   g13.view(E, 2), c2, s2, g2)
+        return cls(w_router_bf16, bias, k, rsf, x_gs, h_gs, c13.view(E, 2 * I, H // 2),
+                   s13.view(E, 2 * I // 16, H // 128, 16, 8), g13.view(E, 2), c2, s2, g2)
 
     def _buffers(self, T: int, reap: bool, out_dtype: torch.dtype):
         key = (T, reap, out_dtype)

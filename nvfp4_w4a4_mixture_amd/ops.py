@@ -116,14 +116,19 @@ def nvfp4_quantize_act(x_bf16: torch.Tensor, global_scale: torch.Tensor, codes: 
 
 
 def nvfp4_quantize_weights(w_bf16: torch.Tensor, stream=None):
-    """w_bf16 [batch, rows, cols] -> (codes [batch, rows, cols/2], scales [batch, rows, cols/16], gs [batch])."""
+    """w_bf16 [batch, rows, cols] -> (codes [batch, rows, cols/2], scales, gs [batch]).
+
+    scales are in the tiled weight layout, shaped [batch, rows/16, cols/128, 16, 8]:
+    scales[b, i, j, r, q] is the scale of row 16 i + r, columns 128 j + 16 q .. + 15."""
     _need(w_bf16, "w_bf16", torch.bfloat16)
     if w_bf16.dim() != 3:
         raise ValueError("w_bf16 must be [batch, rows, cols]")
     b, r, c = w_bf16.shape
     dev = w_bf16.device
     codes = torch.empty((b, r, c // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((b, r, c // 16), dtype=torch.uint8, device=dev)
+    if r % 16 or c % 128:
+        raise ValueError("nvfp4_quantize_weights needs rows % 16 == 0 and cols % 128 == 0")
+    scales = torch.empty((b, r // 16, c // 128, 16, 8), dtype=torch.uint8, device=dev)
     gs = torch.empty((b,), dtype=torch.float32, device=dev)
     st = lib().nvfp4_quantize_weights(_p(w_bf16), b, r, c, _p(codes), _p(scales), _p(gs), _stream(stream))
     check(st, "nvfp4_quantize_weights")
@@ -144,10 +149,10 @@ def moe_nvfp4_grouped_ffn(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs
     _need(x_scales, "x_scales", torch.uint8, (T, H // 16))
     _need(x_gs, "x_gs", torch.float32, (1,))
     _need(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, H // 2))
-    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 16))
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I // 16, H // 128, 16, 8))
     _need(w13_gs, "w13_gs", torch.float32, (E, 2))
     _need(w2_codes, "w2_codes", torch.uint8, (E, H, I // 2))
-    _need(w2_scales, "w2_scales", torch.uint8, (E, H, I // 16))
+    _need(w2_scales, "w2_scales", torch.uint8, (E, H // 16, I // 128, 16, 8))
     _need(w2_gs, "w2_gs", torch.float32, (E,))
     _need(h_gs, "h_gs", torch.float32, (E,))
     _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
@@ -176,7 +181,7 @@ def moe_nvfp4_gate_up_swiglu(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13
     E, two_i, h_half = w13_codes.shape
     H, I = 2 * h_half, two_i // 2
     _need(x_codes, "x_codes", torch.uint8, (T, H // 2))
-    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 16))
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I // 16, H // 128, 16, 8))
     dev = x_codes.device
     if h_codes is None:
         h_codes = torch.empty((T * k, I // 2), dtype=torch.uint8, device=dev)

@@ -141,6 +141,16 @@ def check_routing(ids_gpu, w_gpu, ref: dict, rsf: float, E: int) -> int:
     return int((~clear).sum())
 
 
+def untile_weight_scales(s) -> np.ndarray:
+    """Tiled weight scales [..., R/16, K/128, 16, 8] -> row-major [..., R, K/16].
+
+    The tiled layout is an index permutation of the row-major one: scale (r, b)
+    sits at [r // 16, b // 8, r % 16, b % 8]."""
+    s = np.asarray(s)
+    *lead, rt, kt, r16, q8 = s.shape
+    return np.swapaxes(s, -3, -2).reshape(*lead, rt * r16, kt * q8)
+
+
 def oracle_codes(case: Case):
     """Oracle quantization of x: (packed codes [T, H/2], scales [T, H/16])."""
     c, s = onv.quantize(gen.bf16_bits_to_f32(case.x), case.gs_x)

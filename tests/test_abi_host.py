@@ -47,7 +47,7 @@ def test_binding_signatures_cover_header():
 
 
 def test_version(L):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def _route(L, x=P, T=4, H=64, ldx=64, wr=P, bias=P, E=8, k=2, rsf=2.5, ws=P2, wsb=1 << 20):
@@ -83,11 +83,13 @@ def test_quantize_act_validation(L):
 
 def test_quantize_weights_validation(L):
     q = L.nvfp4_quantize_weights
-    assert q(P, 2, 16, 64, P, P, None, None) == NULL
+    assert q(P, 2, 16, 128, P, P, None, None) == NULL
     assert q(P, 2, 16, 40, P, P, P, None) == SHAPE
-    assert q(P, 2, 0, 64, P, P, P, None) == SHAPE
-    assert q(ctypes.c_void_p(0x10008), 2, 16, 64, P, P, P, None) == ALIGN
-    assert q(P, 0, 16, 64, P, P, P, None) == OK
+    assert q(P, 2, 16, 64, P, P, P, None) == SHAPE  # cols % 128 (tiled scales)
+    assert q(P, 2, 24, 128, P, P, P, None) == SHAPE  # rows % 16
+    assert q(P, 2, 0, 128, P, P, P, None) == SHAPE
+    assert q(ctypes.c_void_p(0x10008), 2, 16, 128, P, P, P, None) == ALIGN
+    assert q(P, 0, 16, 128, P, P, P, None) == OK
 
 
 def _ffn(L, T=16, H=256, E=8, I=128, k=2, ws=P2, wsb=1 << 30, xc=P, sq=None, po=P):
@@ -148,3 +150,21 @@ def test_missing_library_fails_loudly(tmp_path):
 
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_tiled_weight_scale_layout():
+    """The tests' untiling helper follows the header's byte formula for tiled weight scales."""
+    import sys
+    import numpy as np
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_cases import untile_weight_scales
+
+    R, K = 48, 384
+    nb = K // 16
+    flat = np.arange(R * nb, dtype=np.int64)  # flat[i] = storage byte index i
+    tiled = flat.reshape(R // 16, K // 128, 16, 8)
+    rm = untile_weight_scales(tiled)  # rm[r, b] = storage index of scale (r, b)
+    for r in range(R):
+        for b in range(nb):
+            assert rm[r, b] == (r // 16) * K + (b // 8) * 128 + (r % 16) * 8 + b % 8

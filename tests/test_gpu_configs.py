@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_cases import bf16_round, check_routing, rel_l2, say, to_np
+from gpu_cases import bf16_round, check_routing, rel_l2, say, to_np, untile_weight_scales
 from oracle import moe as omoe
 from oracle import nvfp4 as onv
 from oracle import routing as oroute
@@ -95,10 +95,12 @@ def test_full_size_workload(ci):
     for e in sorted(wcheck):
         q = experts[e]
         c13, s13, g13 = (to_np(t[e]) for t in layer.w13)
+        s13 = untile_weight_scales(s13)
         assert np.array_equal(c13[:cfg.I], q.gate_codes) and np.array_equal(c13[cfg.I:], q.up_codes)
         assert np.array_equal(s13[:cfg.I], q.gate_scales) and np.array_equal(s13[cfg.I:], q.up_scales)
         assert g13[0] == q.gate_gs and g13[1] == q.up_gs
         c2, s2, g2 = (to_np(t[e]) for t in layer.w2)
+        s2 = untile_weight_scales(s2)
         assert np.array_equal(c2, q.down_codes) and np.array_equal(s2, q.down_scales)
         assert g2 == q.down_gs
 

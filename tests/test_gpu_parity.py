@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from gpu_cases import (bf16_round, check_routing, config_case, dev_bf16, gpu_layer, oracle_codes, oracle_layer,
-                       oracle_perm, random_case, rel_l2, say, to_np)
+                       oracle_perm, random_case, rel_l2, say, to_np, untile_weight_scales)
 from oracle import nvfp4 as onv
 from oracle import routing as oroute
 from workloads import CONFIGS, gen
@@ -40,7 +40,7 @@ def ops():
 def test_library_loaded_in_tree(ops):
     path = ops.lib()._name
     assert os.path.exists(path) and "nvfp4_w4a4_mixture_amd" in path
-    assert ops.lib().moe_abi_version() == 1
+    assert ops.lib().moe_abi_version() == 2
 
 
 # ---------------------------------------------------------------------------
@@ -111,7 +111,7 @@ def test_quantize_weights_bitexact(ops):
     for b in range(3):
         c_ref, s_ref, g_ref = onv.quantize_weight(gen.bf16_bits_to_f32(wb[b]))
         assert to_np(gs)[b] == g_ref
-        assert np.array_equal(to_np(scales)[b], s_ref)
+        assert np.array_equal(untile_weight_scales(to_np(scales))[b], s_ref)
         assert np.array_equal(to_np(codes)[b], c_ref)
     assert to_np(gs)[1] == 1.0
 
@@ -199,6 +199,7 @@ def _layer_check(ops, case, reap=True):
     # weights: GPU RTN == oracle RTN, bitwise
     c13, s13, g13 = (to_np(t) for t in layer.w13)
     c2, s2, g2 = (to_np(t) for t in layer.w2)
+    s13, s2 = untile_weight_scales(s13), untile_weight_scales(s2)
     for e, q in enumerate(case.experts_q):
         assert np.array_equal(c13[e, :case.I], q.gate_codes) and np.array_equal(c13[e, case.I:], q.up_codes)
         assert np.array_equal(s13[e, :case.I], q.gate_scales) and np.array_equal(s13[e, case.I:], q.up_scales)
@@ -249,6 +250,8 @@ def test_layer_parity_config0(ops):
     ("k_equals_e", 17, 256, 128, 4, 4),
     ("many_empty_experts", 40, 256, 128, 256, 8),
     ("tiled_mid", 130, 768, 384, 6, 3),
+    ("stream_decode", 12, 2048, 2048, 8, 2),  # persistent decode kernel: K >= 2048, K % 1024 == 0
+    ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: three K steps per wave and item
 ])
 def test_layer_parity_random(ops, name, T, H, I, E, k):
     case = random_case(name, zlib.crc32(name.encode()) % 1000, T, H, I, E, k)
