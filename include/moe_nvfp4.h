@@ -158,6 +158,8 @@ moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t
  * moe_route; topk_w [T*k].  Requires H % 256 == 0, I % 128 == 0,
  * 1 <= k <= E <= 256.  workspace: moe_ffn_workspace_bytes(...) bytes,
  * 256-byte aligned; it holds the re-quantized h and the tile schedule.
+ * Code arrays, activation scale arrays (x_scales, h_scales) and pair_out
+ * must be 16-byte aligned, weight scale arrays 4-byte aligned.
  * Pairs not listed in sorted_pair_ids are not written. */
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I);
 moe_status moe_nvfp4_grouped_ffn(

@@ -246,9 +246,10 @@ moe_status moe_nvfp4_gate_up_swiglu(const uint8_t* x_codes, const uint8_t* x_sca
   if (!x_codes || !x_scales || !x_gs || !w13_codes || !w13_scales || !w13_gs || !h_gs || !expert_offsets ||
       !sorted_pair_ids || !h_codes || !h_scales)
     return fail(MOE_ERR_NULL, "moe_nvfp4_gate_up_swiglu: a required pointer is NULL");
-  if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(h_codes, 16) || !aligned(x_scales, 4) ||
-      !aligned(w13_scales, 4))
-    return fail(MOE_ERR_ALIGN, "moe_nvfp4_gate_up_swiglu: code arrays must be 16-byte and scale arrays 4-byte aligned");
+  if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(h_codes, 16) || !aligned(x_scales, 16) ||
+      !aligned(h_scales, 16) || !aligned(w13_scales, 4))
+    return fail(MOE_ERR_ALIGN,
+                "moe_nvfp4_gate_up_swiglu: code and activation-scale arrays must be 16-byte, weight scales 4-byte aligned");
   const size_t need = ffn_ws_layout(T, k, E, H, I).total_stage;
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_gate_up_swiglu: workspace needs %zu bytes", need);
@@ -268,9 +269,10 @@ moe_status moe_nvfp4_down_scatter(const uint8_t* h_codes, const uint8_t* h_scale
   if (!h_codes || !h_scales || !h_gs || !w2_codes || !w2_scales || !w2_gs || !expert_offsets || !sorted_pair_ids ||
       !topk_w || !pair_out)
     return fail(MOE_ERR_NULL, "moe_nvfp4_down_scatter: a required pointer is NULL");
-  if (!aligned(h_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) || !aligned(h_scales, 4) ||
+  if (!aligned(h_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) || !aligned(h_scales, 16) ||
       !aligned(w2_scales, 4))
-    return fail(MOE_ERR_ALIGN, "moe_nvfp4_down_scatter: code arrays and pair_out must be 16-byte aligned");
+    return fail(MOE_ERR_ALIGN,
+                "moe_nvfp4_down_scatter: code arrays, h_scales and pair_out must be 16-byte, weight scales 4-byte aligned");
   const size_t need = ffn_ws_layout(T, k, E, H, I).total_stage;
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_down_scatter: workspace needs %zu bytes", need);
@@ -293,8 +295,9 @@ moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales
       !h_gs || !expert_offsets || !sorted_pair_ids || !topk_w || !pair_out)
     return fail(MOE_ERR_NULL, "moe_nvfp4_grouped_ffn: a required pointer is NULL");
   if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) ||
-      !aligned(x_scales, 4) || !aligned(w13_scales, 4) || !aligned(w2_scales, 4))
-    return fail(MOE_ERR_ALIGN, "moe_nvfp4_grouped_ffn: code arrays and pair_out must be 16-byte aligned");
+      !aligned(x_scales, 16) || !aligned(w13_scales, 4) || !aligned(w2_scales, 4))
+    return fail(MOE_ERR_ALIGN,
+                "moe_nvfp4_grouped_ffn: code arrays, x_scales and pair_out must be 16-byte, weight scales 4-byte aligned");
   const FfnWs L = ffn_ws_layout(T, k, E, H, I);
   if (!workspace || workspace_bytes < L.total_full)
     return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_grouped_ffn: workspace needs %zu bytes", L.total_full);

@@ -71,8 +71,12 @@ __device__ __forceinline__ uint32_t load_scales(const uint8_t* p) {
   return *reinterpret_cast<const uint16_t*>(p);
 }
 
+#ifndef MOE_SMALL_WAVES_PER_EU
+#define MOE_SMALL_WAVES_PER_EU 3
+#endif
 template <int MODE, int KB>
-__global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MOE_SMALL_WAVES_PER_EU)))
+void ffn_small_kernel(FfnArgs a) {
   using It = SmallIter<KB>;
   constexpr int kDw = It::kDw;
   const int tile = blockIdx.x;
@@ -80,46 +84,51 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
   const int off = a.offsets[e];
   const int Me = a.offsets[e + 1] - off;
   if (Me <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int64_t K = a.K;
   const int64_t kbytes = K / 2, kscales = K / 16;
 
-  // A row (pair c of this expert); rows past M_e read row off's data with a
-  // zero scale, so they decode to zeros without a branch
+  // Every load is a wave-uniform base that advances with the K iteration
+  // plus a 32-bit lane offset fixed for the whole kernel.
+  // A row (pair c of this expert); rows past M_e read row off's data and take
+  // a zero scale, so they decode to zeros without a branch.
   const bool a_valid = c < Me;
   const int cc = a_valid ? c : 0;
   const int64_t arow = (MODE == kGateUp) ? (int64_t)(a.sorted[off + cc] / a.k) : (int64_t)(off + cc);
-  const uint8_t* a_code_row = a.a_codes + arow * kbytes + g * (KB / 8);
-  const uint8_t* a_scale_row = a.a_scales + arow * kscales + g * (KB / 64);
-  // B rows for the 4 n-subtiles of 16 rows
-  const uint8_t* b_code_row[4];
-  const uint8_t* b_scale_row[4];
+  const uint32_t a_off = (uint32_t)(arow * kbytes) + g * (KB / 8);
+  const uint32_t as_off = (uint32_t)(arow * kscales) + g * (KB / 64);
+  // B: the tile's first row, then rows 16 j + c of the 4 n-subtiles (gate_up:
+  // gate rows for h columns tile*32 + 0..31, then the matching up rows)
+  const int64_t brow0 = (MODE == kGateUp) ? (int64_t)e * 2 * a.I + (int64_t)tile * 32
+                                          : (int64_t)e * a.H + (int64_t)tile * 64;
+  const uint8_t* b_code_base = a.b_codes + brow0 * kbytes;
+  const uint8_t* b_scale_base = a.b_scales + (brow0 >> 4) * K;  // tiled scales, brow0 % 16 == 0
+  uint32_t b_off[4], bs_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t brow;
-    if (MODE == kGateUp) {
-      const int64_t col = (int64_t)tile * 32 + 16 * (j & 1) + c;  // h column
-      brow = (int64_t)e * 2 * a.I + (j < 2 ? 0 : a.I) + col;
-    } else {
-      brow = (int64_t)e * a.H + (int64_t)tile * 64 + 16 * j + c;
-    }
-    b_code_row[j] = a.b_codes + brow * kbytes + g * (KB / 8);
-    // tiled scales: a K iteration of 16 rows is KB contiguous bytes (KB / 128 blocks)
-    b_scale_row[j] = a.b_scales + tiled_scale_index(brow, 0, K) + (KB == 256 ? (g >> 1) * 128 + 4 * (g & 1) : 2 * g);
+    const int64_t r = (MODE == kGateUp ? (j < 2 ? 0 : a.I) + 16 * (j & 1) : 16 * j) + c;
+    b_off[j] = (uint32_t)(r * kbytes) + g * (KB / 8);
+    // a K iteration of a 16-row tile is KB contiguous scale bytes (KB / 128 blocks)
+    bs_off[j] = (uint32_t)((r >> 4) * K + (r & 15) * 8) + (KB == 256 ? (g >> 1) * 128 + 4 * (g & 1) : 2 * g);
   }
 
-  auto load = [&](int64_t it, It& d) {
-    const int64_t cb = it * (KB / 2), sb = it * (KB / 16);
+  auto load = [&](int it, It& d) {
+    const uint8_t* ab = a.a_codes + (int64_t)it * (KB / 2);
+    const uint8_t* asb = a.a_scales + (int64_t)it * (KB / 16);
+    const uint8_t* bb = b_code_base + (int64_t)it * (KB / 2);
+    const uint8_t* bsb = b_scale_base + (int64_t)it * KB;
 #pragma unroll
-    for (int q = 0; q < kDw / 4; ++q) d.ac[q] = *reinterpret_cast<const u32x4_t*>(a_code_row + cb + 16 * q);
-    d.as = a_valid ? load_scales<KB>(a_scale_row + sb) : 0u;
+    for (int q = 0; q < kDw / 4; ++q) d.ac[q] = *reinterpret_cast<const u32x4_t*>(ab + a_off + 16 * q);
+    const uint32_t asv = load_scales<KB>(asb + as_off);
+    d.as = a_valid ? asv : 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int q = 0; q < kDw / 4; ++q)
-        d.bc[j][q] = load_stream(reinterpret_cast<const u32x4_t*>(b_code_row[j] + cb + 16 * q));
-      d.bs[j] = load_scales<KB>(b_scale_row[j] + it * KB);
+        d.bc[j][q] = load_stream(reinterpret_cast<const u32x4_t*>(bb + b_off[j] + 16 * q));
+      d.bs[j] = load_scales<KB>(bsb + bs_off[j]);
     }
   };
 
@@ -142,11 +151,11 @@ __global__ __launch_bounds__(256) void ffn_small_kernel(FfnArgs a) {
   // wave w takes K iterations w, w + 4, ...: at any time the four waves read
   // neighbouring lines of each weight row; the next iteration's loads are in
   // flight while the current one is decoded and multiplied
-  const int64_t nit = K / KB;
+  const int nit = (int)(K / KB);
   if (wave < nit) {
     It cur, nxt;
     load(wave, cur);
-    for (int64_t it = wave; it < nit; it += 4) {
+    for (int it = wave; it < nit; it += 4) {
       if (it + 4 < nit) load(it + 4, nxt);
       compute(cur);
       cur = nxt;

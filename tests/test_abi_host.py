@@ -108,6 +108,8 @@ def test_ffn_validation(L):
     assert _ffn(L, wsb=16) == WORKSPACE
     assert _ffn(L, xc=ctypes.c_void_p(0x10008)) == ALIGN
     assert _ffn(L, po=ctypes.c_void_p(0x10004)) == ALIGN
+    assert L.moe_nvfp4_grouped_ffn(P, ctypes.c_void_p(0x10004), P, 16, 256, P, P, P, P, P, P, P, 8, 128, 2, P, P, P,
+                                   P, None, P2, 1 << 30, None) == ALIGN  # x_scales 16-byte aligned
     assert _ffn(L, ws=ctypes.c_void_p(0x10010)) == ALIGN
     assert _ffn(L, T=0) == OK  # no pairs: no-op
 
