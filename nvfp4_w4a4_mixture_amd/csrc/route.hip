@@ -223,6 +223,138 @@ __global__ __launch_bounds__(256) void route_select_kernel(const double* __restr
   }
 }
 
+// FP64 matrix-core logits.  v_mfma_f64_16x16x4_f64 (16 tokens x 16 experts x 4
+// h per instruction) with each lane's operands converted from BF16 in
+// registers: lane l supplies token row l % 16 of A and expert column l % 16 of
+// B for k = l / 16, and register i of the result is token (l / 16) + 4 i,
+// expert l % 16 (layout checked by a probe on the device).  The sum over k is
+// free to permute as long as A and B agree, so lane group g takes 16
+// contiguous h of every 64-h chunk: two 16-byte loads per row and chunk, no
+// LDS.  Every product of two BF16 values is exact in FP64.
+//   batches (T > 16): a workgroup = 4 waves x 16 tokens over one H range;
+//   decode (T <= 16): a workgroup = 16 tokens over 256 h, wave w takes the
+//   w-th 64-h quarter, and the quarter sums are added in wave order in LDS.
+// Requires H % 16 == 0, ldx % 8 == 0 and 16-byte aligned x and W_r.
+typedef double double4_t __attribute__((ext_vector_type(4)));
+constexpr int kMfmaChunk = 64;
+
+struct MfmaSplit {
+  int64_t nsplit, hlen;
+};
+static MfmaSplit mfma_split(int64_t T, int64_t H) {
+  if (T <= 16) return {(H + 255) / 256, 256};
+  const int64_t blocks = (T + 63) / 64;
+  const int64_t nch = (H + kMfmaChunk - 1) / kMfmaChunk;
+  int64_t ns = (kTargetWGs + blocks - 1) / blocks;
+  ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
+  ns = ns > nch ? nch : ns;
+  const int64_t hlen = ((nch + ns - 1) / ns) * kMfmaChunk;
+  return {(H + hlen - 1) / hlen, hlen};
+}
+
+__device__ __forceinline__ double bf16_pair_elem(const u32x4_t& lo, const u32x4_t& hi, int s) {
+  const uint32_t w = (s < 8 ? lo : hi)[(s >> 1) & 3];
+  return (double)__uint_as_float((s & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+template <int NT, bool SPLIT_H>
+__global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t H,
+                                                                int64_t ldx, const uint16_t* __restrict__ wr, int E,
+                                                                int64_t hlen, double* __restrict__ part) {
+  __shared__ double red[SPLIT_H ? 3 : 1][SPLIT_H ? NT : 1][64][4];
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t split = blockIdx.y;
+  const int64_t t0 = SPLIT_H ? 0 : (int64_t)blockIdx.x * 64 + 16 * wave;
+  const int64_t hs = split * hlen;
+  const int64_t he = hs + hlen < H ? hs + hlen : H;
+  const int64_t hb = SPLIT_H ? hs + kMfmaChunk * wave : hs;
+  const int64_t hend = SPLIT_H ? (hb + kMfmaChunk < he ? hb + kMfmaChunk : he) : he;
+  // this lane's token row and expert rows (clamped; their results are not stored)
+  const int64_t t = t0 + r;
+  const uint16_t* xrow = x + (t < T ? t : T - 1) * ldx + 16 * g;
+  const uint16_t* wrow[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = 16 * n + r;
+    wrow[n] = wr + (int64_t)(e < E ? e : E - 1) * H + 16 * g;
+  }
+  double4_t acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = double4_t{0.0, 0.0, 0.0, 0.0};
+  struct Chunk {
+    u32x4_t a[2];
+    u32x4_t b[NT][2];
+  };
+  auto load = [&](int64_t h0, Chunk& d) {
+    const bool in = h0 + 16 * g < hend;  // H % 16 == 0: a lane group's 16 h are all in or all out
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    d.a[0] = in ? *reinterpret_cast<const u32x4_t*>(xrow + h0) : z;
+    d.a[1] = in ? *reinterpret_cast<const u32x4_t*>(xrow + h0 + 8) : z;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      d.b[n][0] = in ? *reinterpret_cast<const u32x4_t*>(wrow[n] + h0) : z;
+      d.b[n][1] = in ? *reinterpret_cast<const u32x4_t*>(wrow[n] + h0 + 8) : z;
+    }
+  };
+  auto compute = [&](const Chunk& d) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const double av = bf16_pair_elem(d.a[0], d.a[1], s);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bf16_pair_elem(d.b[n][0], d.b[n][1], s), acc[n], 0, 0, 0);
+    }
+  };
+  if (hb < hend) {
+    Chunk cur, nxt;
+    load(hb, cur);
+    for (int64_t h0 = hb; h0 < hend; h0 += kMfmaChunk) {
+      if (h0 + kMfmaChunk < hend) load(h0 + kMfmaChunk, nxt);
+      compute(cur);
+      cur = nxt;
+    }
+  }
+  if (SPLIT_H) {
+    if (wave > 0) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][n][lane][i] = acc[n][i];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[n][i] = ((acc[n][i] + red[0][n][lane][i]) + red[1][n][lane][i]) + red[2][n][lane][i];
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = 16 * n + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tt = t0 + g + 4 * i;
+      if (tt < T && e < E) part[(split * T + tt) * E + e] = acc[n][i];
+    }
+  }
+}
+
+template <int NT, bool SPLIT_H>
+static void launch_logits_mfma(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, int E,
+                               MfmaSplit sp, double* part, hipStream_t st) {
+  const dim3 grid(SPLIT_H ? 1u : (unsigned)((T + 63) / 64), (unsigned)sp.nsplit);
+  hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E, sp.hlen,
+                     part);
+}
+
+// Smallest instantiated n-tile count covering E experts (E <= 256).
+static int mfma_nt(int E) {
+  const int need = (E + 15) / 16;
+  return need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : need <= 5 ? 5 : need <= 8 ? 8 : 16;
+}
+
 // Decode batches (T <= kDecT).  Logits: each workgroup takes kDecH hidden
 // elements for up to 64 experts; wave w takes the w-th quarter of that range,
 // lane = expert, with the lane's 64 router weights in registers and the tokens'
@@ -487,6 +619,7 @@ size_t route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k) {
   const RouteSplit sp = route_split(T, H);
   int64_t nsplit = sp.nsplit;
   if (T <= kDecT && dec_nsplit(H) > nsplit) nsplit = dec_nsplit(H);
+  if (mfma_split(T, H).nsplit > nsplit) nsplit = mfma_split(T, H).nsplit;
   return align256((size_t)(2 * nchunks * E * 4)) + (size_t)(nsplit * T * E * 8);
 }
 
@@ -512,23 +645,47 @@ hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, co
   double* part = reinterpret_cast<double*>(static_cast<unsigned char*>(workspace) +
                                            align256((size_t)(2 * nchunks * E * 4)));
   const bool vec16 = (H % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)wr % 16 == 0);
-  if (T <= kDecT && vec16) {
-    const int64_t ns = dec_nsplit(H);
-    hipLaunchKernelGGL(route_logits_decode_kernel, dim3((unsigned)ns, (unsigned)((e + 63) / 64)), dim3(256), 0, st,
+  const int nt = mfma_nt(e);
+  const bool mfma = vec16 && H % 16 == 0 && (T > kDecT || nt <= 8);
+  int64_t nsplit = 0;
+  if (mfma) {
+    const MfmaSplit ms = mfma_split(T, H);
+    nsplit = ms.nsplit;
+    const bool split_h = T <= kDecT;
+#define LM(N)                                                                  \
+  case N:                                                                      \
+    if (split_h) launch_logits_mfma<N, true>(x, T, H, ldx, wr, e, ms, part, st); \
+    else launch_logits_mfma<N, false>(x, T, H, ldx, wr, e, ms, part, st);        \
+    break;
+    switch (nt) {
+      LM(1) LM(2) LM(4) LM(5) LM(8)
+      case 16:  // decode batches with E > 128 take the register/LDS kernel above (mfma is false there)
+        launch_logits_mfma<16, false>(x, T, H, ldx, wr, e, ms, part, st);
+        break;
+      default: return hipErrorInvalidValue;
+    }
+#undef LM
+  } else if (T <= kDecT && vec16) {
+    nsplit = dec_nsplit(H);
+    hipLaunchKernelGGL(route_logits_decode_kernel, dim3((unsigned)nsplit, (unsigned)((e + 63) / 64)), dim3(256), 0, st,
                        x, T, H, ldx, wr, e, part);
-    hipLaunchKernelGGL(route_select_permute_decode_kernel, dim3(1), dim3(1024), 0, st, part, ns, T, bias, e, kk, rsf,
-                       topk_ids, topk_w, counts, offsets, sorted);
-    return hipGetLastError();
-  }
-  const RouteSplit sp = route_split(T, H);
-  switch ((e + 15) / 16) {
+  } else {
+    const RouteSplit sp = route_split(T, H);
+    nsplit = sp.nsplit;
+    switch ((e + 15) / 16) {
 #define LG(N) \
   case N: launch_logits<N>(x, T, H, ldx, wr, e, sp, part, st); break;
-    LG(1) LG(2) LG(3) LG(4) LG(5) LG(6) LG(7) LG(8) LG(9) LG(10) LG(11) LG(12) LG(13) LG(14) LG(15) LG(16)
+      LG(1) LG(2) LG(3) LG(4) LG(5) LG(6) LG(7) LG(8) LG(9) LG(10) LG(11) LG(12) LG(13) LG(14) LG(15) LG(16)
 #undef LG
-    default: return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
-  hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, part, sp.nsplit, T, bias,
+  if (T <= kDecT) {
+    hipLaunchKernelGGL(route_select_permute_decode_kernel, dim3(1), dim3(1024), 0, st, part, nsplit, T, bias, e, kk,
+                       rsf, topk_ids, topk_w, counts, offsets, sorted);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, part, nsplit, T, bias,
                      e, kk, rsf, topk_ids, topk_w);
   hipLaunchKernelGGL(perm_count_kernel, dim3(nchunks), dim3(256), 0, st, topk_ids, npairs, e, chunk_counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, st, chunk_counts, nchunks, e, chunk_base, counts,
