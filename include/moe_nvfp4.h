@@ -113,6 +113,18 @@ moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
                      int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pair_ids,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_route and nvfp4_quantize_act(x, T, H, ldx, x_gs, x_codes, x_scales) in
+ * one call: the routing pass that reads x also writes its NVFP4 codes
+ * [T, H/2] and scales [T, H/16] (bit-identical to nvfp4_quantize_act).
+ * Requirements of both calls apply (H % 16 == 0, ldx % 8 == 0, x 16-byte
+ * aligned, x_codes 8-byte aligned); same workspace as moe_route. */
+moe_status moe_route_quantize(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
+                              const uint16_t* w_router_bf16, const float* bias, int64_t E, int64_t k,
+                              float routed_scaling_factor, const float* x_gs, uint8_t* x_codes,
+                              uint8_t* x_scales, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                              int32_t* expert_offsets, int32_t* sorted_pair_ids, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Dynamic NVFP4 quantization of BF16 activations against a calibrated,
  * static global scale ("K-EXAONE-152B-A23B-REAP-80E-NVFP4" model card,

@@ -31,6 +31,8 @@ SIGNATURES = {
     "moe_abi_version": (_i32, []),
     "moe_route_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "moe_route": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_route_quantize": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _i64, _f32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  _p, _sz, _p]),
     "nvfp4_quantize_act": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "nvfp4_quantize_weights": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "moe_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),

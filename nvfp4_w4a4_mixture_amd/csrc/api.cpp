@@ -107,27 +107,55 @@ size_t moe_route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k) {
   return moe::route_workspace_bytes(T, H, E, k);
 }
 
+// Shared body of moe_route and moe_route_quantize (qcodes == NULL: no quantization).
+static moe_status route_impl(const char* fn, const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
+                             const uint16_t* w_router_bf16, const float* bias, int64_t E, int64_t k, float rsf,
+                             const float* x_gs, uint8_t* x_codes, uint8_t* x_scales, int32_t* topk_ids, float* topk_w,
+                             int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pair_ids,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w_router_bf16 || !bias || !expert_counts || !expert_offsets ||
+      (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !sorted_pair_ids)))
+    return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (T < 0 || H < 1 || ldx < H) return fail(MOE_ERR_SHAPE, "%s: need T >= 0, H >= 1, ldx >= H", fn);
+  if (k < 1 || E < k || E > 256) return fail(MOE_ERR_SHAPE, "%s: need 1 <= k <= E <= 256", fn);
+  if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "%s: T*k must be < 2^31", fn);
+  if (!(rsf > 0.0f)) return fail(MOE_ERR_SHAPE, "%s: routed_scaling_factor must be > 0", fn);
+  if (x_codes) {
+    if (H % 16 != 0) return fail(MOE_ERR_SHAPE, "%s: H must be a multiple of 16 to quantize x", fn);
+    if (T > 0 && (!x_gs || !x_scales)) return fail(MOE_ERR_NULL, "%s: x_gs and x_scales are required", fn);
+    if (T > 0 && (ldx % 8 != 0 || !aligned(x_bf16, 16) || !aligned(x_codes, 8)))
+      return fail(MOE_ERR_ALIGN, "%s: x must be 16-byte aligned with ldx %% 8 == 0; x_codes 8-byte aligned", fn);
+  }
+  const size_t need = moe::route_workspace_bytes(T, H, E, k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (need > 0 && !aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  if (moe_status s = check_device()) return s;
+  // T == 0 still writes zero counts and offsets.
+  return launched(moe::launch_route(x_bf16, T, H, ldx, w_router_bf16, bias, E, k, rsf, topk_ids, topk_w,
+                                    expert_counts, expert_offsets, sorted_pair_ids, workspace, x_gs,
+                                    T > 0 ? x_codes : nullptr, x_scales, (hipStream_t)stream),
+                  fn);
+}
+
 moe_status moe_route(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx, const uint16_t* w_router_bf16,
                      const float* bias, int64_t E, int64_t k, float routed_scaling_factor, int32_t* topk_ids,
                      float* topk_w, int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pair_ids,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  if (!w_router_bf16 || !bias || !expert_counts || !expert_offsets ||
-      (T > 0 && (!x_bf16 || !topk_ids || !topk_w || !sorted_pair_ids)))
-    return fail(MOE_ERR_NULL, "moe_route: a required pointer is NULL");
-  if (T < 0 || H < 1 || ldx < H) return fail(MOE_ERR_SHAPE, "moe_route: need T >= 0, H >= 1, ldx >= H");
-  if (k < 1 || E < k || E > 256) return fail(MOE_ERR_SHAPE, "moe_route: need 1 <= k <= E <= 256");
-  if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "moe_route: T*k must be < 2^31");
-  if (!(routed_scaling_factor > 0.0f)) return fail(MOE_ERR_SHAPE, "moe_route: routed_scaling_factor must be > 0");
-  const size_t need = moe::route_workspace_bytes(T, H, E, k);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace needs %zu bytes", need);
-  if (need > 0 && !aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "moe_route: workspace must be 256-byte aligned");
-  if (moe_status s = check_device()) return s;
-  // T == 0 still writes zero counts and offsets.
-  return launched(moe::launch_route(x_bf16, T, H, ldx, w_router_bf16, bias, E, k, routed_scaling_factor, topk_ids,
-                                    topk_w, expert_counts, expert_offsets, sorted_pair_ids, workspace,
-                                    (hipStream_t)stream),
-                  "moe_route");
+  return route_impl("moe_route", x_bf16, T, H, ldx, w_router_bf16, bias, E, k, routed_scaling_factor, nullptr,
+                    nullptr, nullptr, topk_ids, topk_w, expert_counts, expert_offsets, sorted_pair_ids, workspace,
+                    workspace_bytes, stream);
+}
+
+moe_status moe_route_quantize(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
+                              const uint16_t* w_router_bf16, const float* bias, int64_t E, int64_t k,
+                              float routed_scaling_factor, const float* x_gs, uint8_t* x_codes, uint8_t* x_scales,
+                              int32_t* topk_ids, float* topk_w, int32_t* expert_counts, int32_t* expert_offsets,
+                              int32_t* sorted_pair_ids, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T > 0 && !x_codes) return fail(MOE_ERR_NULL, "moe_route_quantize: x_codes is NULL");
+  return route_impl("moe_route_quantize", x_bf16, T, H, ldx, w_router_bf16, bias, E, k, routed_scaling_factor, x_gs,
+                    T > 0 ? x_codes : nullptr, x_scales, topk_ids, topk_w, expert_counts, expert_offsets,
+                    sorted_pair_ids, workspace, workspace_bytes, stream);
 }
 
 moe_status nvfp4_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols, int64_t ld,

@@ -43,7 +43,8 @@ hipError_t launch_weight_global_scales(const uint16_t* w, int64_t batch, int64_t
 size_t route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k);
 hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, const float* bias,
                         int64_t E, int64_t k, float rsf, int32_t* topk_ids, float* topk_w, int32_t* counts,
-                        int32_t* offsets, int32_t* sorted, void* workspace, hipStream_t st);
+                        int32_t* offsets, int32_t* sorted, void* workspace, const float* qgs, uint8_t* qcodes,
+                        uint8_t* qscales, hipStream_t st);
 
 int64_t ffn_max_tiles(int64_t T, int64_t k, int64_t E);
 int ffn_sq_parts(int64_t H);

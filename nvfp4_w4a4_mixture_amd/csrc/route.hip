@@ -257,10 +257,16 @@ __device__ __forceinline__ double bf16_pair_elem(const u32x4_t& lo, const u32x4_
   return (double)__uint_as_float((s & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
-template <int NT, bool SPLIT_H>
+// QUANT: every lane also writes the NVFP4 quantization of its 16 x values (one
+// block) to codes [T, H/2] and scales [T, H/16] against the global scale *qgs
+// (the same steps as nvfp4_quantize_act); the grid covers each block once.
+template <int NT, bool SPLIT_H, bool QUANT>
 __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t H,
                                                                 int64_t ldx, const uint16_t* __restrict__ wr, int E,
-                                                                int64_t hlen, double* __restrict__ part) {
+                                                                int64_t hlen, double* __restrict__ part,
+                                                                const float* __restrict__ qgs,
+                                                                uint8_t* __restrict__ qcodes,
+                                                                uint8_t* __restrict__ qscales) {
   __shared__ double red[SPLIT_H ? 3 : 1][SPLIT_H ? NT : 1][64][4];
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -297,6 +303,23 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
       d.b[n][1] = in ? *reinterpret_cast<const u32x4_t*>(wrow[n] + h0 + 8) : z;
     }
   };
+  const float gsq = QUANT ? qgs[0] : 0.0f;
+  auto quantize = [&](int64_t h0, const Chunk& d) {
+    if (t < T && h0 + 16 * g < hend) {
+      float f[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w = d.a[i >> 2][i & 3];
+        f[2 * i] = bf16_to_f32(w & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(w >> 16);
+      }
+      uint32_t lo, hi;
+      const uint32_t sc = quantize_block16(f, gsq, lo, hi);
+      const int64_t hblk = h0 + 16 * g;
+      *reinterpret_cast<uint2*>(qcodes + t * (H / 2) + hblk / 2) = make_uint2(lo, hi);
+      qscales[t * (H / 16) + hblk / 16] = (uint8_t)sc;
+    }
+  };
   auto compute = [&](const Chunk& d) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
@@ -311,6 +334,7 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
     load(hb, cur);
     for (int64_t h0 = hb; h0 < hend; h0 += kMfmaChunk) {
       if (h0 + kMfmaChunk < hend) load(h0 + kMfmaChunk, nxt);
+      if (QUANT) quantize(h0, cur);
       compute(cur);
       cur = nxt;
     }
@@ -343,10 +367,15 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
 
 template <int NT, bool SPLIT_H>
 static void launch_logits_mfma(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, int E,
-                               MfmaSplit sp, double* part, hipStream_t st) {
+                               MfmaSplit sp, double* part, const float* qgs, uint8_t* qcodes, uint8_t* qscales,
+                               hipStream_t st) {
   const dim3 grid(SPLIT_H ? 1u : (unsigned)((T + 63) / 64), (unsigned)sp.nsplit);
-  hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E, sp.hlen,
-                     part);
+  if (qcodes)
+    hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H, true>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E,
+                       sp.hlen, part, qgs, qcodes, qscales);
+  else
+    hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H, false>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E,
+                       sp.hlen, part, qgs, qcodes, qscales);
 }
 
 // Smallest instantiated n-tile count covering E experts (E <= 256).
@@ -632,7 +661,8 @@ static void launch_logits(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, 
 
 hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, const float* bias,
                         int64_t E, int64_t k, float rsf, int32_t* topk_ids, float* topk_w, int32_t* counts,
-                        int32_t* offsets, int32_t* sorted, void* workspace, hipStream_t st) {
+                        int32_t* offsets, int32_t* sorted, void* workspace, const float* qgs, uint8_t* qcodes,
+                        uint8_t* qscales, hipStream_t st) {
   const int e = (int)E, kk = (int)k;
   const int64_t npairs = T * k;
   const int nchunks = (int)((npairs + kPermChunk - 1) / kPermChunk);
@@ -654,30 +684,36 @@ hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, co
     const bool split_h = T <= kDecT;
 #define LM(N)                                                                  \
   case N:                                                                      \
-    if (split_h) launch_logits_mfma<N, true>(x, T, H, ldx, wr, e, ms, part, st); \
-    else launch_logits_mfma<N, false>(x, T, H, ldx, wr, e, ms, part, st);        \
+    if (split_h) launch_logits_mfma<N, true>(x, T, H, ldx, wr, e, ms, part, qgs, qcodes, qscales, st); \
+    else launch_logits_mfma<N, false>(x, T, H, ldx, wr, e, ms, part, qgs, qcodes, qscales, st);        \
     break;
     switch (nt) {
       LM(1) LM(2) LM(4) LM(5) LM(8)
-      case 16:  // decode batches with E > 128 take the register/LDS kernel above (mfma is false there)
-        launch_logits_mfma<16, false>(x, T, H, ldx, wr, e, ms, part, st);
+      case 16:  // only batches: decode batches with E > 128 take the register/LDS kernel (mfma is false there)
+        launch_logits_mfma<16, false>(x, T, H, ldx, wr, e, ms, part, qgs, qcodes, qscales, st);
         break;
       default: return hipErrorInvalidValue;
     }
 #undef LM
-  } else if (T <= kDecT && vec16) {
-    nsplit = dec_nsplit(H);
-    hipLaunchKernelGGL(route_logits_decode_kernel, dim3((unsigned)nsplit, (unsigned)((e + 63) / 64)), dim3(256), 0, st,
-                       x, T, H, ldx, wr, e, part);
   } else {
-    const RouteSplit sp = route_split(T, H);
-    nsplit = sp.nsplit;
-    switch ((e + 15) / 16) {
+    if (qcodes) {  // these logits kernels do not quantize: a separate pass
+      const hipError_t err = launch_quantize_bf16(x, T, H, ldx, qgs, T, qcodes, qscales, false, st);
+      if (err != hipSuccess) return err;
+    }
+    if (T <= kDecT && vec16) {
+      nsplit = dec_nsplit(H);
+      hipLaunchKernelGGL(route_logits_decode_kernel, dim3((unsigned)nsplit, (unsigned)((e + 63) / 64)), dim3(256), 0,
+                         st, x, T, H, ldx, wr, e, part);
+    } else {
+      const RouteSplit sp = route_split(T, H);
+      nsplit = sp.nsplit;
+      switch ((e + 15) / 16) {
 #define LG(N) \
   case N: launch_logits<N>(x, T, H, ldx, wr, e, sp, part, st); break;
-      LG(1) LG(2) LG(3) LG(4) LG(5) LG(6) LG(7) LG(8) LG(9) LG(10) LG(11) LG(12) LG(13) LG(14) LG(15) LG(16)
+        LG(1) LG(2) LG(3) LG(4) LG(5) LG(6) LG(7) LG(8) LG(9) LG(10) LG(11) LG(12) LG(13) LG(14) LG(15) LG(16)
 #undef LG
-      default: return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+      }
     }
   }
   if (T <= kDecT) {

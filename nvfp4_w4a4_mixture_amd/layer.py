@@ -82,7 +82,7 @@ class NVFP4MoELayer:
             self._bufs[key] = b
         return b
 
-    STAGES = ("route", "quantize", "gate_up", "down", "combine", "reap")
+    STAGES = ("route_quantize", "gate_up", "down", "combine", "reap")
 
     def forward(self, x_bf16: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, reap: bool = False,
                 events: Optional[list] = None) -> LayerOut:
@@ -92,26 +92,27 @@ class NVFP4MoELayer:
         b = self._buffers(T, reap, out_dtype)
         mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
         mark(0)
-        r = ops.moe_route(x_bf16, self.w_router, self.bias, self.k, self.rsf, out=b["route"], workspace=b["route_ws"])
+        # routing and the NVFP4 quantization of x in one pass over x
+        r, _, _ = ops.moe_route_quantize(x_bf16, self.w_router, self.bias, self.k, self.rsf, self.x_gs,
+                                         out=b["route"], x_codes=b["x_codes"], x_scales=b["x_scales"],
+                                         workspace=b["route_ws"])
         mark(1)
-        ops.nvfp4_quantize_act(x_bf16, self.x_gs, b["x_codes"], b["x_scales"])
-        mark(2)
         # the two stages of moe_nvfp4_grouped_ffn, called separately so each can be timed
         ops.moe_nvfp4_gate_up_swiglu(b["x_codes"], b["x_scales"], self.x_gs, *self.w13, self.h_gs, self.k,
                                      r.expert_offsets, r.sorted_pair_ids, b["h_codes"], b["h_scales"],
                                      workspace=b["ffn_ws"])
-        mark(3)
+        mark(2)
         ops.moe_nvfp4_down_scatter(b["h_codes"], b["h_scales"], self.h_gs, T, *self.w2, self.k, r.expert_offsets,
                                    r.sorted_pair_ids, r.topk_w, pair_out=b["pair_out"],
                                    pair_sqnorm=b["pair_sqnorm"] if reap else None, workspace=b["ffn_ws"])
-        mark(4)
+        mark(3)
         ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
-        mark(5)
+        mark(4)
         sal = None
         if reap:
             sal = ops.reap_saliency(b["pair_sqnorm"], r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, self.k,
                                     self.E, out=b["saliency"])
-        mark(6)
+        mark(5)
         return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal)
 
     __call__ = forward

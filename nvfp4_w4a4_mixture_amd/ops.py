@@ -15,7 +15,7 @@ import torch
 
 from ._lib import MoEError, check, lib  # noqa: F401
 
-__all__ = ["moe_route", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
+__all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
            "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
            "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
 
@@ -94,6 +94,43 @@ def moe_route(x_bf16: torch.Tensor, w_router_bf16: torch.Tensor, bias: torch.Ten
                          _p(out.expert_offsets), _p(out.sorted_pair_ids), _p(ws), ws.numel(), _stream(stream))
     check(st, "moe_route")
     return out
+
+
+def moe_route_quantize(x_bf16: torch.Tensor, w_router_bf16: torch.Tensor, bias: torch.Tensor, k: int,
+                       routed_scaling_factor: float, x_gs: torch.Tensor, out: Optional[RouteOut] = None,
+                       x_codes: Optional[torch.Tensor] = None, x_scales: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """moe_route plus the NVFP4 quantization of x in the same pass: (RouteOut, x_codes, x_scales)."""
+    if x_bf16.dim() != 2 or (x_bf16.numel() > 0 and x_bf16.stride(1) != 1):
+        raise ValueError("x_bf16 must be [T, H] with unit column stride")
+    _need(x_bf16, "x_bf16", torch.bfloat16, contiguous=False)
+    T, H = x_bf16.shape
+    ldx = x_bf16.stride(0) if T > 0 else H
+    E = w_router_bf16.shape[0]
+    _need(w_router_bf16, "w_router_bf16", torch.bfloat16, (E, H))
+    _need(bias, "bias", torch.float32, (E,))
+    _need(x_gs, "x_gs", torch.float32, (1,))
+    dev = x_bf16.device
+    if out is None:
+        out = RouteOut(torch.empty((T, k), dtype=torch.int32, device=dev),
+                       torch.empty((T, k), dtype=torch.float32, device=dev),
+                       torch.empty((E,), dtype=torch.int32, device=dev),
+                       torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                       torch.empty((T * k,), dtype=torch.int32, device=dev))
+    if x_codes is None:
+        x_codes = torch.empty((T, H // 2), dtype=torch.uint8, device=dev)
+    if x_scales is None:
+        x_scales = torch.empty((T, H // 16), dtype=torch.uint8, device=dev)
+    _need(x_codes, "x_codes", torch.uint8, (T, H // 2))
+    _need(x_scales, "x_scales", torch.uint8, (T, H // 16))
+    nbytes = moe_route_workspace_bytes(T, H, E, k)
+    ws = _workspace(nbytes, dev, workspace)
+    st = lib().moe_route_quantize(_p(x_bf16), T, H, ldx, _p(w_router_bf16), _p(bias), E, k,
+                                  float(routed_scaling_factor), _p(x_gs), _p(x_codes), _p(x_scales),
+                                  _p(out.topk_ids), _p(out.topk_w), _p(out.expert_counts), _p(out.expert_offsets),
+                                  _p(out.sorted_pair_ids), _p(ws), ws.numel(), _stream(stream))
+    check(st, "moe_route_quantize")
+    return out, x_codes, x_scales
 
 
 def nvfp4_quantize_act(x_bf16: torch.Tensor, global_scale: torch.Tensor, codes: Optional[torch.Tensor] = None,

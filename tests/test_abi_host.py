@@ -69,6 +69,22 @@ def test_route_validation(L):
     assert b"moe_route" in L.moe_last_error()
 
 
+def test_route_quantize_validation(L):
+    rq = L.moe_route_quantize
+
+    def call(x=P, T=4, H=64, ldx=64, codes=P, scales=P, gs=P):
+        return rq(x, T, H, ldx, P, P, 8, 2, 2.5, gs, codes, scales, P, P, P, P, P, P2, 1 << 20, None)
+
+    assert call(codes=None) == NULL
+    assert call(gs=None) == NULL
+    assert call(scales=None) == NULL
+    assert call(H=40, ldx=40) == SHAPE  # H % 16
+    assert call(ldx=68) == ALIGN  # ldx % 8
+    assert call(x=ctypes.c_void_p(0x10008)) == ALIGN
+    assert call(codes=ctypes.c_void_p(0x10004)) == ALIGN
+    assert b"moe_route_quantize" in L.moe_last_error()
+
+
 def test_quantize_act_validation(L):
     q = L.nvfp4_quantize_act
     assert q(None, 4, 64, 64, P, P, P, None) == NULL

@@ -170,6 +170,31 @@ def test_route_strided_rows(ops, T, H, pad):
     assert np.array_equal(to_np(out.sorted_pair_ids), p_ref)
 
 
+@pytest.mark.parametrize("T,H,E,k", [(16, 6144, 80, 8), (300, 512, 80, 8), (16, 1024, 256, 8), (1, 256, 8, 2),
+                                     (70, 768, 128, 4)])
+# (16, 1024, 256, 8): decode batch with E > 128 takes the register/LDS logits kernel and a separate quantize pass
+def test_route_quantize_matches_route_and_quantize(ops, T, H, E, k):
+    say(f"route_quantize T={T} H={H} E={E} k={k}")
+    rng = np.random.default_rng(T * 7 + H + E)
+    xb = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wr = gen.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    g = float(np.float32(2688.0 / np.abs(gen.bf16_bits_to_f32(xb)).max()))
+    gs = torch.tensor([g], dtype=torch.float32, device="cuda")
+    out, codes, scales = ops.moe_route_quantize(dev_bf16(xb), dev_bf16(wr), torch.from_numpy(bias).cuda(), k, 2.5, gs)
+    torch.cuda.synchronize()
+    c_ref, s_ref = onv.quantize(gen.bf16_bits_to_f32(xb), np.float32(g))
+    assert np.array_equal(to_np(codes), onv.pack_codes(c_ref))
+    assert np.array_equal(to_np(scales), s_ref)
+    ids = to_np(out.topk_ids)
+    ref = dict(zip(("ids", "weights", "weights64", "gap"), oroute.route(xb, wr, bias, k, 2.5)))
+    assert check_routing(ids, to_np(out.topk_w), ref, 2.5, E) == 0
+    c_ref, o_ref, p_ref = oracle_perm(ids, E)
+    assert np.array_equal(to_np(out.expert_counts), c_ref)
+    assert np.array_equal(to_np(out.expert_offsets), o_ref)
+    assert np.array_equal(to_np(out.sorted_pair_ids), p_ref)
+
+
 @pytest.mark.parametrize("T", [12, 40, 200])  # decode path, general path (one and several chunks)
 def test_route_exact_ties_go_to_lower_index(ops, T):
     say(f"route crafted ties T={T}")
