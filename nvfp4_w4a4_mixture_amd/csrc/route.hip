@@ -5,21 +5,23 @@
 // top-8 routing; "K-EXAONE-152B-A23B-REAP-80E-NVFP4", "Quantization Setup":
 // the router stays BF16).
 //
-// route_logits_kernel: FP64 logit partials for a 64-token tile over one range
-// of the hidden dimension, from BF16 x and W_r staged through LDS (every
-// product and sum is FP64).  route_select_kernel: one wave per token sums the
-// partials in a fixed order and ranks every expert under (score descending,
-// expert ascending); rank < k is slot `rank` of the top-k.  Selection decides
+// Logits: FP64 partial sums over ranges of H, on the FP64 matrix cores
+// (route_logits_mfma_kernel) when rows are 16-byte aligned and H % 16 == 0,
+// else on the vector units (route_logits_kernel for batches,
+// route_logits_decode_kernel for T <= 16).  Every product of two BF16 values
+// is exact in FP64.  The MFMA kernel can also write the NVFP4 quantization of
+// x, which it holds in registers anyway (moe_route_quantize).
+//
+// Selection (route_select_kernel): one wave per token sums the partials in
+// split order and ranks every expert under (score descending, expert
+// ascending); rank < k is slot `rank` of the top-k.  Selection decides
 // integers, so it runs in FP64 like the definition it follows; ties go to the
 // lower expert index.
 //
-// The permutation is a stable counting sort in three passes over chunks of
-// kPermChunk pairs: per-chunk histograms, a per-expert scan over chunks, and a
-// per-chunk scatter that ranks equal experts by pair id with wave ballots.
-//
-// Decode batches (T <= 16) take two kernels instead: logits over 256-wide
-// hidden slices with the router weights in registers, then selection and the
-// whole counting sort in one workgroup.
+// Permutation: a stable counting sort, in one workgroup for up to 16 tokens
+// (perm_small_kernel), else in three passes over chunks of kPermChunk
+// pairs: per-chunk histograms, a per-expert scan over chunks, and a per-chunk
+// scatter that ranks equal experts by pair id with wave ballots.
 #include "device_common.h"
 #include "launch.h"
 
@@ -454,98 +456,56 @@ __global__ __launch_bounds__(256) void route_logits_decode_kernel(const uint16_t
   }
 }
 
-// Decode batches: logits, selection and the whole stable counting sort in one
-// workgroup of 16 waves.  First every thread reduces (token, expert) partial
-// sums in split order with the loads of up to 32 splits in flight, into an
-// LDS row per token; then wave t selects for token t from its row.
-// slot[t][e] = 1 + the top-k slot in which token t chose expert e (0: not
-// chosen); a pair's rank inside its expert is the number of earlier tokens
-// that chose the same expert, which is the order of pair ids.
-template <int NG>
-__device__ __forceinline__ void select_decode_token(double* row, const float* bias_l, int64_t t, int E, int k,
-                                                    float rsf, int lane, int32_t* __restrict__ topk_ids,
-                                                    float* __restrict__ topk_w, int (&slot)[4]) {
-  double sg[NG], sc[NG];
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    const int e = lane + 64 * i < E ? lane + 64 * i : E - 1;
-    sg[i] = 1.0 / (1.0 + exp(-row[e]));
-    sc[i] = sg[i] + (double)bias_l[e];
-  }
-  wave_lds_sync();  // logits read before rank_select overwrites the row
-  rank_select<NG>(sg, sc, t, E, k, rsf, lane, row, topk_ids, topk_w, slot);
-}
-
-__global__ __launch_bounds__(1024) void route_select_permute_decode_kernel(
-    const double* __restrict__ part, int64_t nsplit, int64_t T, const float* __restrict__ bias, int E, int k,
-    float rsf, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted) {
-  constexpr int kBatch = 32;
-  __shared__ __align__(16) double rows[kDecT][258];
-  __shared__ float bias_l[256];
-  __shared__ uint16_t slot[kDecT][256];
+// Stable counting sort of a decode batch (T <= 16 tokens) in one workgroup,
+// parallel over pairs p = t * k + j: each pair marks sel[t][e] and counts its
+// expert (integer LDS atomics: order-free); an exclusive scan over experts
+// gives the offsets; a pair's rank inside its expert is the number of earlier
+// tokens that chose the same expert (a token never picks an expert twice),
+// which is the order of pair ids.
+constexpr int kSmallPermT = 16;
+__global__ __launch_bounds__(256) void perm_small_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ sorted) {
+  __shared__ uint32_t sel[kSmallPermT][256 / 4];  // bytes sel[t][e]
+  __shared__ int32_t cnt[256];
+  __shared__ int32_t base[256];
   __shared__ int32_t wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kDecT * 256; i += 1024) (&slot[0][0])[i] = 0;
-  if (tid < E) bias_l[tid] = bias[tid];
-  const int64_t npe = T * E;
-  for (int64_t p = tid; p < npe; p += 1024) {
-    const double* pp = part + p;  // part[(s * T + t) * E + e] = pp[s * T * E] with p = t * E + e
-    double z = 0.0;
-    for (int64_t s0 = 0; s0 < nsplit; s0 += kBatch) {
-      double v[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int64_t sj = s0 + j < nsplit ? s0 + j : nsplit - 1;
-        v[j] = pp[sj * npe];
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        if (s0 + j < nsplit) z += v[j];
-    }
-    const int64_t t = p / E;
-    rows[t][p - t * E] = z;
+  const int npairs = T * k;
+  for (int i = tid; i < kSmallPermT * 64; i += 256) (&sel[0][0])[i] = 0u;
+  cnt[tid] = 0;
+  __syncthreads();
+  uint8_t* selb = reinterpret_cast<uint8_t*>(&sel[0][0]);
+  for (int p = tid; p < npairs; p += 256) {
+    const int e = ids[p];
+    selb[(p / k) * 256 + e] = 1;
+    atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (wave < T) {
-    int sl[4];
-    const int64_t t = wave;
-    switch ((E + 63) >> 6) {
-      case 1: select_decode_token<1>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
-      case 2: select_decode_token<2>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
-      case 3: select_decode_token<3>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
-      default: select_decode_token<4>(rows[t], bias_l, t, E, k, rsf, lane, topk_ids, topk_w, sl); break;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) slot[t][lane + 64 * i] = (uint16_t)sl[i];
-  }
-  __syncthreads();
-  // per-expert counts and an exclusive scan over experts (threads 0..255)
-  int cnt = 0;
-  if (tid < E)
-    for (int t = 0; t < T; ++t) cnt += (slot[t][tid] != 0);
-  int incl = cnt;
+  const int c = tid < E ? cnt[tid] : 0;
+  int incl = c;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int n = __shfl_up(incl, off);
     if (lane >= off) incl += n;
   }
-  if (lane == 63 && wave < 4) wsum[wave] = incl;
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   int pre = 0;
-  for (int w = 0; w < wave && w < 4; ++w) pre += wsum[w];
-  const int base = pre + incl - cnt;
+  for (int w = 0; w < wave; ++w) pre += wsum[w];
   if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = base;
-    int r = base;
-    for (int t = 0; t < T; ++t) {
-      const int sl = slot[t][tid];
-      if (sl) sorted[r++] = (int32_t)(t * k + sl - 1);
-    }
+    counts[tid] = c;
+    offsets[tid] = pre + incl - c;
+    base[tid] = pre + incl - c;
   }
   if (tid == 0) offsets[E] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  for (int p = tid; p < npairs; p += 256) {
+    const int e = ids[p], t = p / k;
+    int r = 0;
+    for (int t2 = 0; t2 < t; ++t2) r += selb[t2 * 256 + e];
+    sorted[base[e] + r] = p;
+  }
 }
 
 // Per-chunk expert histograms: counts[c][e] for chunk c of kPermChunk pairs.
@@ -716,13 +676,12 @@ hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, co
       }
     }
   }
-  if (T <= kDecT) {
-    hipLaunchKernelGGL(route_select_permute_decode_kernel, dim3(1), dim3(1024), 0, st, part, nsplit, T, bias, e, kk,
-                       rsf, topk_ids, topk_w, counts, offsets, sorted);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, st, part, nsplit, T, bias,
                      e, kk, rsf, topk_ids, topk_w);
+  if (T <= kSmallPermT) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(256), 0, st, topk_ids, (int)T, kk, e, counts, offsets, sorted);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(perm_count_kernel, dim3(nchunks), dim3(256), 0, st, topk_ids, npairs, e, chunk_counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(256), 0, st, chunk_counts, nchunks, e, chunk_base, counts,
                      offsets);

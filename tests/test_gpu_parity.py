@@ -119,8 +119,9 @@ def test_quantize_weights_bitexact(ops):
 # ---------------------------------------------------------------------------
 # routing + permutation
 
-# T <= 16 with 16-byte aligned rows takes the decode kernels (H-sliced logits, one-workgroup select+permute);
-# larger batches the tiled logits and the chunked counting sort
+# Logits: FP64 MFMA kernel when rows are 16-byte aligned and H % 16 == 0 (H-split across waves for T <= 16,
+# E <= 128), else the vector kernels (H = 520: register/LDS decode kernel; E = 256 at T = 16: same).
+# Permutation: one workgroup up to 16 tokens, else the chunked counting sort.
 @pytest.mark.parametrize("T,H,E,k", [(64, 256, 8, 2), (300, 512, 80, 8), (1000, 256, 128, 8), (37, 64, 256, 16),
                                      (5, 32, 1, 1), (3, 32, 16, 16), (2500, 128, 80, 8), (0, 64, 8, 2),
                                      (64, 64, 128, 16), (16, 6144, 80, 8), (16, 6144, 256, 256), (13, 520, 200, 9)])
