@@ -301,49 +301,56 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
       return (int64_t)e * a.H + (int64_t)nt * BN + n;
     }
   };
+  // DMA sources: a wave-uniform base per operand that advances with the stage
+  // plus a 32-bit lane offset fixed for the kernel (B offsets are relative to
+  // the expert's first row).
   // 16-byte code DMA i of this wave: rows 16 q .. 16 q + 15 with q = 4 i + wave;
   // lane -> row 16 q + lane / 4, LDS slot lane % 4 holding chunk slot ^ ((row >> 2) & 3)
-  const uint8_t* a_code_src[S::kACodeOps];
-  const uint8_t* b_code_src[S::kBCodeOps];
+  const int64_t erow0 = MODE == kGateUp ? (int64_t)e * 2 * a.I : (int64_t)e * a.H;  // expert's first B row
+  const uint8_t* b_code_expert = a.b_codes + erow0 * kbytes;
+  const uint8_t* b_scale_expert = a.b_scales + (erow0 >> 4) * K;  // tiled scales; erow0 % 16 == 0
+  uint32_t a_code_off[S::kACodeOps], b_code_off[S::kBCodeOps];
 #pragma unroll
   for (int i = 0; i < S::kACodeOps; ++i) {
     const int row = 16 * (4 * i + wave) + (lane >> 2);
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    a_code_src[i] = a.a_codes + a_row(row) * kbytes + 16 * chunk;
+    a_code_off[i] = (uint32_t)(a_row(row) * kbytes) + 16 * chunk;
   }
 #pragma unroll
   for (int i = 0; i < S::kBCodeOps; ++i) {
     const int row = 16 * (4 * i + wave) + (lane >> 2);
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    b_code_src[i] = a.b_codes + b_row(row) * kbytes + 16 * chunk;
+    b_code_off[i] = (uint32_t)((b_row(row) - erow0) * kbytes) + 16 * chunk;
   }
   // 4-byte scale DMA i of this wave: rows 32 q .. 32 q + 31, q = 4 i + wave; lane -> row 32 q + lane / 2, dword lane % 2
-  const uint8_t* a_scale_src[S::kAScaleOps];
-  const uint8_t* b_scale_src[S::kBScaleOps];
+  uint32_t a_scale_off[S::kAScaleOps], b_scale_off[S::kBScaleOps];
 #pragma unroll
   for (int i = 0; i < S::kAScaleOps; ++i) {
     const int row = 32 * (4 * i + wave) + (lane >> 1);
-    a_scale_src[i] = a.a_scales + a_row(row) * kscales + 4 * (lane & 1);
+    a_scale_off[i] = (uint32_t)(a_row(row) * kscales) + 4 * (lane & 1);
   }
 #pragma unroll
   for (int i = 0; i < S::kBScaleOps; ++i) {
-    const int row = 32 * (4 * i + wave) + (lane >> 1);
-    b_scale_src[i] = a.b_scales + tiled_scale_index(b_row(row), 0, K) + 4 * (lane & 1);  // tiled: 128 B per stage
+    const int64_t br = b_row(32 * (4 * i + wave) + (lane >> 1)) - erow0;
+    b_scale_off[i] = (uint32_t)tiled_scale_index(br, 0, K) + 4 * (lane & 1);  // tiled: 128 B per stage
   }
 
   auto issue = [&](int64_t st) {
     unsigned char* base = smem + (int)(st % NS) * S::kStage;
-    const int64_t cbo = st * 64, sbo = st * 8;  // 128 k per stage
+    const uint8_t* ac = a.a_codes + st * 64;  // 128 k per stage
+    const uint8_t* as = a.a_scales + st * 8;
+    const uint8_t* bc = b_code_expert + st * 64;
+    const uint8_t* bs = b_scale_expert + st * 128;
 #pragma unroll
-    for (int i = 0; i < S::kACodeOps; ++i) dma16(a_code_src[i] + cbo, base + (4 * i + wave) * 1024);
+    for (int i = 0; i < S::kACodeOps; ++i) dma16(ac + a_code_off[i], base + (4 * i + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < S::kAScaleOps; ++i) dma4(a_scale_src[i] + sbo, base + S::kACodeBytes + (4 * i + wave) * 256);
+    for (int i = 0; i < S::kAScaleOps; ++i) dma4(as + a_scale_off[i], base + S::kACodeBytes + (4 * i + wave) * 256);
 #pragma unroll
     for (int i = 0; i < S::kBCodeOps; ++i)
-      dma16(b_code_src[i] + cbo, base + S::kACodeBytes + S::kAScaleBytes + (4 * i + wave) * 1024);
+      dma16(bc + b_code_off[i], base + S::kACodeBytes + S::kAScaleBytes + (4 * i + wave) * 1024);
 #pragma unroll
     for (int i = 0; i < S::kBScaleOps; ++i)
-      dma4(b_scale_src[i] + st * 128, base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes + (4 * i + wave) * 256);
+      dma4(bs + b_scale_off[i], base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes + (4 * i + wave) * 256);
   };
 
   float16_t acc[WM][WN];
@@ -385,54 +392,93 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     asm volatile("" ::: "memory");
     if (st + NS - 1 < nst) issue(st + NS - 1);
     const unsigned char* base = smem + (int)(st % NS) * S::kStage;
-    // this lane's operand words of stage st: code fragments [q][i] (A) and
-    // [q][j] (B), 16 B each, and one scale word per fragment row
-    u32x4_t fa[2][WM], fb[2][WN];
-    uint32_t sa[WM], sbv[WN];
     if constexpr (WM == 4 && WN == 4) {
-      // All reads of the stage in one asm block ending in its own lgkmcnt(0).
-      // Issued by the compiler, an LDS read after the in-flight ring DMA would
-      // get a conservative vmcnt(0) (it cannot tell the ring stages apart),
-      // draining the DMA of the later stages too.  Fragment i of a row block
-      // sits 2048 B (32 rows) after fragment i-1; its scale word 256 B after.
+      // The stage's LDS reads in two asm blocks (k 0..63, then k 64..127), each
+      // ending in its own lgkmcnt(0).  Issued by the compiler, an LDS read after
+      // the in-flight ring DMA would get a conservative vmcnt(0) (it cannot tell
+      // the ring stages apart), draining the DMA of the later stages too.
+      // Fragment i of a row block sits 2048 B (32 rows) after fragment i-1; its
+      // scale word 256 B after.
       const uint32_t sb = lds_base + (uint32_t)(st % NS) * S::kStage;
       const uint32_t a0 = sb + a_lane + 16u * slot_q0, a1 = sb + a_lane + 16u * slot_q1;
       const uint32_t b0 = sb + b_lane + 16u * slot_q0, b1 = sb + b_lane + 16u * slot_q1;
       const uint32_t as_addr = sb + as_lane, bs_addr = sb + bs_lane;
+      u32x4_t fa[4], fb[4];
+      uint32_t sa[4], sbv[4];
       asm volatile(
-          "ds_read_b32 %16, %28 offset:0\n"
-          "ds_read_b32 %17, %28 offset:256\n"
-          "ds_read_b32 %18, %28 offset:512\n"
-          "ds_read_b32 %19, %28 offset:768\n"
-          "ds_read_b32 %20, %29 offset:0\n"
-          "ds_read_b32 %21, %29 offset:256\n"
-          "ds_read_b32 %22, %29 offset:512\n"
-          "ds_read_b32 %23, %29 offset:768\n"
-          "ds_read_b128 %0, %24 offset:0\n"
-          "ds_read_b128 %1, %24 offset:2048\n"
-          "ds_read_b128 %2, %24 offset:4096\n"
-          "ds_read_b128 %3, %24 offset:6144\n"
-          "ds_read_b128 %4, %26 offset:0\n"
-          "ds_read_b128 %5, %26 offset:2048\n"
-          "ds_read_b128 %6, %26 offset:4096\n"
-          "ds_read_b128 %7, %26 offset:6144\n"
-          "ds_read_b128 %8, %25 offset:0\n"
-          "ds_read_b128 %9, %25 offset:2048\n"
-          "ds_read_b128 %10, %25 offset:4096\n"
-          "ds_read_b128 %11, %25 offset:6144\n"
-          "ds_read_b128 %12, %27 offset:0\n"
-          "ds_read_b128 %13, %27 offset:2048\n"
-          "ds_read_b128 %14, %27 offset:4096\n"
-          "ds_read_b128 %15, %27 offset:6144\n"
+          "ds_read_b32 %8, %18 offset:0\n"
+          "ds_read_b32 %9, %18 offset:256\n"
+          "ds_read_b32 %10, %18 offset:512\n"
+          "ds_read_b32 %11, %18 offset:768\n"
+          "ds_read_b32 %12, %19 offset:0\n"
+          "ds_read_b32 %13, %19 offset:256\n"
+          "ds_read_b32 %14, %19 offset:512\n"
+          "ds_read_b32 %15, %19 offset:768\n"
+          "ds_read_b128 %0, %16 offset:0\n"
+          "ds_read_b128 %1, %16 offset:2048\n"
+          "ds_read_b128 %2, %16 offset:4096\n"
+          "ds_read_b128 %3, %16 offset:6144\n"
+          "ds_read_b128 %4, %17 offset:0\n"
+          "ds_read_b128 %5, %17 offset:2048\n"
+          "ds_read_b128 %6, %17 offset:4096\n"
+          "ds_read_b128 %7, %17 offset:6144\n"
           "s_waitcnt lgkmcnt(0)\n"
-          : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[0][2]), "=&v"(fa[0][3]), "=&v"(fb[0][0]),
-            "=&v"(fb[0][1]), "=&v"(fb[0][2]), "=&v"(fb[0][3]), "=&v"(fa[1][0]), "=&v"(fa[1][1]),
-            "=&v"(fa[1][2]), "=&v"(fa[1][3]), "=&v"(fb[1][0]), "=&v"(fb[1][1]), "=&v"(fb[1][2]),
-            "=&v"(fb[1][3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sbv[0]),
-            "=&v"(sbv[1]), "=&v"(sbv[2]), "=&v"(sbv[3])
-          : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(as_addr), "v"(bs_addr)
+          : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
+            "=&v"(fb[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sbv[0]), "=&v"(sbv[1]),
+            "=&v"(sbv[2]), "=&v"(sbv[3])
+          : "v"(a0), "v"(b0), "v"(as_addr), "v"(bs_addr)
           : "memory");
+      // Sub-steps ss = 0..7 (q = ss / 4 half, s = ss % 4 dword): the operands of
+      // sub-step ss + 1 are decoded while the 16 MFMAs of sub-step ss run.
+      half8_t da[2][4], db[2][4];
+      auto decode_step = [&](int ss, int buf) {
+        const int sbyte = 2 * (ss >> 2) + ((ss & 3) >> 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][ss & 3], scale_pair(sa[i], sbyte));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) db[buf][j] = decode8(fb[j][ss & 3], scale_pair(sbv[j], sbyte));
+      };
+      auto mfma_step = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[buf][i], db[buf][j], acc[i][j], 0, 0, 0);
+      };
+      decode_step(0, 0);
+#pragma unroll
+      for (int ss = 0; ss < 8; ++ss) {
+        const int cur = ss & 1;
+        if (ss == 3) {
+          asm volatile(
+              "ds_read_b128 %0, %8 offset:0\n"
+              "ds_read_b128 %1, %8 offset:2048\n"
+              "ds_read_b128 %2, %8 offset:4096\n"
+              "ds_read_b128 %3, %8 offset:6144\n"
+              "ds_read_b128 %4, %9 offset:0\n"
+              "ds_read_b128 %5, %9 offset:2048\n"
+              "ds_read_b128 %6, %9 offset:4096\n"
+              "ds_read_b128 %7, %9 offset:6144\n"
+              "s_waitcnt lgkmcnt(0)\n"
+              : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
+                "=&v"(fb[3])
+              : "v"(a1), "v"(b1)
+              : "memory");
+        }
+        if (ss + 1 < 8) decode_step(ss + 1, cur ^ 1);
+        mfma_step(cur);
+        // schedule: each of the 16 MFMAs followed by a slice of the next decode
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        }
+      }
     } else {
+      // this lane's operand words of stage st: code fragments [q][i] (A) and
+      // [q][j] (B), 16 B each, and one scale word per fragment row
+      u32x4_t fa[2][WM], fb[2][WN];
+      uint32_t sa[WM], sbv[WN];
       const uint32_t* as = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes);
       const uint32_t* bsc = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes);
       const u32x4_t* ac = reinterpret_cast<const u32x4_t*>(base);
@@ -450,21 +496,22 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 #pragma unroll
         for (int j = 0; j < WN; ++j) fb[q][j] = bc[(wn * 32 * WN + 32 * j + r) * 4 + slot];
       }
-    }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < 2; ++q) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int sbyte = 2 * q + (s >> 1);
-        half8_t af[WM], bf[WN];
+        for (int s = 0; s < 4; ++s) {
+          const int sbyte = 2 * q + (s >> 1);
+          half8_t af[WM], bf[WN];
 #pragma unroll
-        for (int i = 0; i < WM; ++i) af[i] = decode8(fa[q][i][s], scale_pair(sa[i], sbyte));
+          for (int i = 0; i < WM; ++i) af[i] = decode8(fa[q][i][s], scale_pair(sa[i], sbyte));
 #pragma unroll
-        for (int j = 0; j < WN; ++j) bf[j] = decode8(fb[q][j][s], scale_pair(sbv[j], sbyte));
+          for (int j = 0; j < WN; ++j) bf[j] = decode8(fb[q][j][s], scale_pair(sbv[j], sbyte));
 #pragma unroll
-        for (int i = 0; i < WM; ++i)
+          for (int i = 0; i < WM; ++i)
 #pragma unroll
-          for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < WN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
