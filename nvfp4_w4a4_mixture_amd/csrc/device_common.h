@@ -112,7 +112,13 @@ __device__ __forceinline__ half2_t scale_pair(uint32_t scales4, int k) {
   return h * k256;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g) from the hardware base-2 exponential and reciprocal
+// (about 1 ulp each); for very negative g, 2^x overflows to +inf and the
+// result is -0.
+__device__ __forceinline__ float silu(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // Weight block scales are stored tiled: the 16 x 8 scale bytes of 16
 // consecutive rows and 128 consecutive columns form one 128-byte block

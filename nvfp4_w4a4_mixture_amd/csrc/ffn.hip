@@ -552,6 +552,15 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     }
   } else {
     float* sqbuf = reinterpret_cast<float*>(smem + (S::kLds - 2 * BM * 4));
+    // the tile's pair ids and weights, staged once in the (now free) ring
+    int32_t* prow = reinterpret_cast<int32_t*>(smem);
+    float* wrow = reinterpret_cast<float*>(smem + BM * 4);
+    for (int t = tid; t < BM; t += 256) {
+      const int32_t p = t < rows_here ? a.sorted[off + row0 + t] : 0;
+      prow[t] = p;
+      wrow[t] = t < rows_here ? a.topk_w[p] : 0.0f;
+    }
+    __syncthreads();
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
@@ -559,13 +568,9 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
       for (int q = 0; q < 16; ++q) {
         const int row = wm * 32 * WM + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3);
         float ss = 0.0f;
-        int64_t p = 0;
-        float wp = 0.0f;
         const bool ok = row < rows_here;
-        if (ok) {
-          p = a.sorted[off + row0 + row];
-          wp = a.topk_w[p];
-        }
+        const int64_t p = prow[row];
+        const float wp = wrow[row];
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const float f = acc[i][j][q] * alpha;
@@ -578,10 +583,8 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
       }
     }
     __syncthreads();
-    if (a.sq_part != nullptr && tid < BM && tid < rows_here) {
-      const int64_t p = a.sorted[off + row0 + tid];
-      a.sq_part[p * a.n_part + nt] = sqbuf[tid] + sqbuf[BM + tid];
-    }
+    if (a.sq_part != nullptr && tid < BM && tid < rows_here)
+      a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = sqbuf[tid] + sqbuf[BM + tid];
   }
 }
 
