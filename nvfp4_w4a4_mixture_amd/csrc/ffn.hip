@@ -114,6 +114,12 @@ void ffn_small_kernel(FfnArgs a) {
     bs_off[j] = (uint32_t)((r >> 4) * K + (r & 15) * 8) + (KB == 256 ? (g >> 1) * 128 + 4 * (g & 1) : 2 * g);
   }
 
+  // down epilogue: the output row of thread tid (pair tid / 16) and its weight,
+  // loaded now so that the epilogue does not wait for them
+  const int erow = tid >> 4;
+  const int64_t ep_pair = (MODE == kDown && erow < Me) ? (int64_t)a.sorted[off + erow] : 0;
+  const float ep_w = (MODE == kDown && erow < Me) ? a.topk_w[ep_pair] : 0.0f;
+
   auto load = [&](int it, It& d) {
     const uint8_t* ab = a.a_codes + (int64_t)it * (KB / 2);
     const uint8_t* asb = a.a_scales + (int64_t)it * (KB / 16);
@@ -203,23 +209,21 @@ void ffn_small_kernel(FfnArgs a) {
       }
     }
   } else {
-    const int row = tid >> 4, q = tid & 15;  // 4 consecutive columns per thread
+    const int q = tid & 15;  // 4 consecutive columns per thread, row erow
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
     float f[4];
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[i] = tilebuf[row][4 * q + i] * alpha;
+      f[i] = tilebuf[erow][4 * q + i] * alpha;
       ss += f[i] * f[i];
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 16);
-    if (row < Me) {
-      const int64_t p = a.sorted[off + row];
-      const float wp = a.topk_w[p];
-      float4 out = make_float4(wp * f[0], wp * f[1], wp * f[2], wp * f[3]);
-      *reinterpret_cast<float4*>(a.pair_out + p * a.H + (int64_t)tile * 64 + 4 * q) = out;
-      if (a.sq_part != nullptr && q == 0) a.sq_part[p * a.n_part + tile] = ss;
+    if (erow < Me) {
+      float4 out = make_float4(ep_w * f[0], ep_w * f[1], ep_w * f[2], ep_w * f[3]);
+      *reinterpret_cast<float4*>(a.pair_out + ep_pair * a.H + (int64_t)tile * 64 + 4 * q) = out;
+      if (a.sq_part != nullptr && q == 0) a.sq_part[ep_pair * a.n_part + tile] = ss;
     }
   }
 }
