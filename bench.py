@@ -37,11 +37,14 @@ FFN_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_mixture_amd", "csrc", "ffn.hip")
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = decode-shaped layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4, help="tokens in the oracle's timed sample")
+    ap.add_argument("--union-sweep", action="store_true",
+                    help="decode only: time the layer on the first T tokens for T = 1, 2, 4, 8, 16 and report the "
+                         "experts touched, weight bytes streamed and tokens/s (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) to calibrate HBM counters")
     return ap.parse_args(argv)
@@ -93,6 +96,33 @@ def read_traffic(kernel: str, workload: str):
     if not m or not h or h.group(1) != ffn_source_hash():
         return None
     return float(m.group(1))
+
+
+def union_sweep(cfg, layer, x, steps: int, warmup: int) -> dict:
+    """Small-batch decode: the union of the experts the T tokens touch sets the bytes streamed per step."""
+    import numpy as np
+    import torch
+
+    per_expert = stage_bytes_flops(cfg, np.ones(cfg.E))["gate_up"]["per_expert_bytes"] + \
+        stage_bytes_flops(cfg, np.ones(cfg.E))["down"]["per_expert_bytes"]
+    rows = []
+    for T in (1, 2, 4, 8, 16):
+        if T > x.shape[0]:
+            break
+        xt = x[:T].contiguous()
+        for _ in range(warmup):
+            layer(xt, out_dtype=torch.bfloat16, reap=False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            out = layer(xt, out_dtype=torch.bfloat16, reap=False)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / steps
+        touched = int(np.count_nonzero(out.route.expert_counts.cpu().numpy()))
+        wbytes = touched * per_expert
+        rows.append({"tokens": T, "experts_touched": touched, "weight_bytes": int(wbytes), "ms_per_step": sec * 1e3,
+                     "tokens_per_s": T / sec, "weight_GB_per_s": wbytes / sec / 1e9})
+    return {"study": "decode expert union", "workload": cfg.name, "steps": steps, "warmup": warmup, "rows": rows}
 
 
 def cpu_baseline(cfg, n_tokens: int) -> dict:
@@ -168,6 +198,9 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
     stages = layer.STAGES
+    if args.union_sweep:
+        print(json.dumps(union_sweep(cfg, layer, x, args.steps, args.warmup)), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         layer(x, out_dtype=torch.bfloat16, reap=True)
