@@ -45,6 +45,10 @@ def parse_args(argv=None):
     ap.add_argument("--union-sweep", action="store_true",
                     help="decode only: time the layer on the first T tokens for T = 1, 2, 4, 8, 16 and report the "
                          "experts touched, weight bytes streamed and tokens/s (one JSON line)")
+    ap.add_argument("--reap-prune", type=int, default=0, metavar="N_KEEP",
+                    help="REAP one-shot pruning study on --config (3 = the 128-expert layer): saliency from one "
+                         "pass, prune to N_KEEP experts, output drift against the unpruned layer for the REAP, a "
+                         "seeded random, the lowest-saliency and the most-routed choice, prune time and step times (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) to calibrate HBM counters")
     return ap.parse_args(argv)
@@ -125,6 +129,72 @@ def union_sweep(cfg, layer, x, steps: int, warmup: int) -> dict:
     return {"study": "decode expert union", "workload": cfg.name, "steps": steps, "warmup": warmup, "rows": rows}
 
 
+def _step_ms(layer, x, steps: int, warmup: int) -> float:
+    import torch
+
+    for _ in range(warmup):
+        layer(x, out_dtype=torch.bfloat16, reap=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer(x, out_dtype=torch.bfloat16, reap=False)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def reap_prune_study(cfg, layer, x, n_keep: int, steps: int, warmup: int) -> dict:
+    """REAP one-shot pruning: rank the saliency of one pass, keep n_keep experts, measure the output drift."""
+    import numpy as np
+    import torch
+
+    from nvfp4_w4a4_mixture_amd import ops
+
+    full = layer(x, out_dtype=torch.float32, reap=True)
+    y_full = full.y.clone()
+    sal = full.saliency.clone()
+    counts = full.route.expert_counts.cpu().numpy()
+    torch.cuda.synchronize()
+    # time the pruning itself: the selection and the gathers of every per-expert tensor
+    prune_ms = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pl = layer.prune(sal, n_keep)
+        e1.record()
+        torch.cuda.synchronize()
+        prune_ms.append(e0.elapsed_time(e1))
+    tensors = [pl.w_router, pl.bias, pl.h_gs, *pl.w13, *pl.w2]
+    moved = sum(t.numel() * t.element_size() for t in tensors)
+    keeps = {"reap": pl.keep_ids}
+    rng = np.random.default_rng(n_keep)
+    keeps["random"] = torch.from_numpy(np.sort(rng.choice(cfg.E, n_keep, replace=False)).astype(np.int32)).cuda()
+    keeps["lowest_saliency"] = torch.from_numpy(
+        np.sort(np.argsort(sal.cpu().numpy(), kind="stable")[:n_keep]).astype(np.int32)).cuda()
+    # frequency pruning, for contrast: keep the experts that receive the most pairs
+    keeps["most_routed"] = torch.from_numpy(
+        np.sort(np.argsort(-counts, kind="stable")[:n_keep]).astype(np.int32)).cuda()
+    den = torch.linalg.vector_norm(y_full.double())
+    rows = []
+    for name, keep in keeps.items():
+        p = pl if name == "reap" else layer.take_experts(keep)
+        out = p(x, out_dtype=torch.float32)
+        drift = float(torch.linalg.vector_norm(out.y.double() - y_full.double()) / den)
+        kept = np.zeros(cfg.E, bool)
+        kept[keep.cpu().numpy()] = True
+        rows.append({"choice": name, "y_rel_l2_drift": drift,
+                     "pairs_rerouted_frac": float(counts[~kept].sum() / counts.sum()),
+                     "kept_saliency_sum_frac": float(sal.cpu().numpy()[kept].sum() / sal.cpu().numpy().sum())})
+        del p, out
+    ms_full = _step_ms(layer, x, steps, warmup)
+    ms_pruned = _step_ms(pl, x, steps, warmup)
+    return {"study": "REAP one-shot pruning", "workload": cfg.name, "experts": cfg.E, "kept": n_keep,
+            "tokens": cfg.T, "prune_ms": float(np.median(prune_ms)), "prune_bytes_gathered": int(moved),
+            "prune_GB_per_s_rw": 2 * moved / (np.median(prune_ms) / 1e3) / 1e9, "rows": rows,
+            "step_ms_unpruned": ms_full, "step_ms_pruned": ms_pruned,
+            "tokens_per_s_unpruned": cfg.T / ms_full * 1e3, "tokens_per_s_pruned": cfg.T / ms_pruned * 1e3,
+            "steps": steps, "warmup": warmup}
+
+
 def cpu_baseline(cfg, n_tokens: int) -> dict:
     """The oracle on a bounded sample of the same workload (the first n_tokens tokens)."""
     import numpy as np
@@ -200,6 +270,9 @@ def main(argv=None) -> int:
     stages = layer.STAGES
     if args.union_sweep:
         print(json.dumps(union_sweep(cfg, layer, x, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.reap_prune:
+        print(json.dumps(reap_prune_study(cfg, layer, x, args.reap_prune, args.steps, args.warmup)), flush=True)
         return 0
 
     for _ in range(args.warmup):

@@ -221,6 +221,36 @@ moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w,
                          const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                          int64_t T, int64_t k, int64_t E, float* saliency, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* REAP one-shot pruning ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card,
+ * introduction and "Pruning Setup": the routed experts of lowest REAP
+ * saliency are removed, 128 -> 80 per layer; the router's gate weight and
+ * e_score_correction_bias are sliced to the experts that remain and the
+ * renormalized sigmoid routing is kept).
+ *
+ * reap_prune_select: keep_ids [n_keep] INT32 receives the n_keep experts of
+ * highest saliency, in ascending index order.  Experts are ranked by
+ * (saliency descending, index ascending): among equal saliencies the lower
+ * index is kept, and -0 equals +0.  saliency [E] FP32 (from reap_saliency;
+ * an expert never routed to has saliency 0 and is removed first).  For a NaN
+ * saliency the result is still n_keep distinct ascending ids (NaN orders by
+ * its bits), but which ones is unspecified.  1 <= n_keep <= E <= 256;
+ * 4-byte aligned pointers. */
+moe_status reap_prune_select(const float* saliency, int64_t E, int64_t n_keep, int32_t* keep_ids,
+                             void* stream);
+
+/* moe_gather_experts: slices one per-expert tensor of a layer to the kept
+ * experts -- dst block i (bytes_per_expert bytes) = src block keep_ids[i].
+ * Every per-expert tensor of the layer is such a sequence of contiguous
+ * blocks: w13/w2 codes (2I*H/2 and H*I/2 bytes), their tiled scales (2I*H/16
+ * and H*I/16 bytes), w13_gs (8), w2_gs (4), h_gs (4), router rows (2H) and
+ * bias (4).  src holds E_src blocks, dst n_keep blocks; the two must not
+ * overlap.  A keep_ids entry outside [0, E_src) leaves its dst block
+ * unwritten.  1 <= n_keep <= 65535; keep_ids 4-byte aligned.  16-byte loads
+ * and stores are used when src, dst and bytes_per_expert are multiples of 16. */
+moe_status moe_gather_experts(const void* src, int64_t E_src, int64_t bytes_per_expert,
+                              const int32_t* keep_ids, int64_t n_keep, void* dst, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -365,6 +366,33 @@ moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w, const in
   return launched(moe::launch_reap(pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids, E, saliency,
                                    (hipStream_t)stream),
                   "reap_saliency");
+}
+
+moe_status reap_prune_select(const float* saliency, int64_t E, int64_t n_keep, int32_t* keep_ids, void* stream) {
+  if (E < 1 || E > 256 || n_keep < 1 || n_keep > E)
+    return fail(MOE_ERR_SHAPE, "reap_prune_select: need 1 <= n_keep <= E <= 256 (n_keep=%lld, E=%lld)",
+                (long long)n_keep, (long long)E);
+  if (!saliency || !keep_ids) return fail(MOE_ERR_NULL, "reap_prune_select: a required pointer is NULL");
+  if (!aligned(saliency, 4) || !aligned(keep_ids, 4))
+    return fail(MOE_ERR_ALIGN, "reap_prune_select: 4-byte alignment required");
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_prune_select(saliency, E, n_keep, keep_ids, (hipStream_t)stream), "reap_prune_select");
+}
+
+moe_status moe_gather_experts(const void* src, int64_t E_src, int64_t bytes_per_expert, const int32_t* keep_ids,
+                              int64_t n_keep, void* dst, void* stream) {
+  if (E_src < 1 || bytes_per_expert < 1 || n_keep < 1 || n_keep > 65535)
+    return fail(MOE_ERR_SHAPE, "moe_gather_experts: need E_src >= 1, bytes_per_expert >= 1, 1 <= n_keep <= 65535");
+  if (E_src > INT64_MAX / bytes_per_expert || n_keep > INT64_MAX / bytes_per_expert)
+    return fail(MOE_ERR_SHAPE, "moe_gather_experts: total size overflows");
+  if (!src || !dst || !keep_ids) return fail(MOE_ERR_NULL, "moe_gather_experts: a required pointer is NULL");
+  if (!aligned(keep_ids, 4)) return fail(MOE_ERR_ALIGN, "moe_gather_experts: keep_ids must be 4-byte aligned");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t s1 = s0 + (uintptr_t)(E_src * bytes_per_expert), d1 = d0 + (uintptr_t)(n_keep * bytes_per_expert);
+  if (s0 < d1 && d0 < s1) return fail(MOE_ERR_SHAPE, "moe_gather_experts: src and dst overlap");
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_gather_blocks(src, E_src, bytes_per_expert, keep_ids, n_keep, dst, (hipStream_t)stream),
+                  "moe_gather_experts");
 }
 
 }  // extern "C"

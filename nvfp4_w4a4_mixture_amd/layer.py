@@ -1,6 +1,6 @@
 """The routed NVFP4 W4A4 MoE layer as one object: the C-ABI calls in order.
 
-forward(x):  moe_route -> nvfp4_quantize_act -> moe_nvfp4_gate_up_swiglu ->
+forward(x):  moe_route_quantize -> moe_nvfp4_gate_up_swiglu ->
              moe_nvfp4_down_scatter -> moe_combine (-> reap_saliency)
 (the two FFN calls are the stages of moe_nvfp4_grouped_ffn)
 All buffers for a given token count are allocated once and reused, so a
@@ -43,6 +43,7 @@ class NVFP4MoELayer:
         self.H, self.I = 2 * h_half, two_i // 2
         self.device = w13_codes.device
         self._bufs: dict = {}
+        self.keep_ids = None  # set on a layer made by prune(): its experts' ids in the unpruned layer
 
     @classmethod
     def from_bf16(cls, w_router_bf16, bias, k, rsf, x_gs, h_gs, w13_bf16, w2_bf16):
@@ -81,6 +82,23 @@ class NVFP4MoELayer:
             )
             self._bufs[key] = b
         return b
+
+    def prune(self, saliency: torch.Tensor, n_keep: int) -> "NVFP4MoELayer":
+        """REAP one-shot pruning: a new layer with the n_keep highest-saliency experts.
+
+        The router rows, the bias and every expert tensor are sliced to the
+        kept experts, in ascending original index ("K-EXAONE-152B-A23B-REAP-80E-BF16"
+        model card, "Pruning Setup").  The kept ids are in ``.keep_ids``."""
+        return self.take_experts(ops.reap_prune_select(saliency, n_keep))
+
+    def take_experts(self, keep_ids: torch.Tensor) -> "NVFP4MoELayer":
+        """A new layer whose expert i is this layer's expert keep_ids[i] (INT32 on the device):
+        router rows, bias, calibrated h global scales and every expert tensor gathered."""
+        g = lambda t: ops.moe_gather_experts(t, keep_ids)  # noqa: E731
+        out = NVFP4MoELayer(g(self.w_router), g(self.bias), self.k, self.rsf, self.x_gs, g(self.h_gs),
+                            *(g(t) for t in self.w13), *(g(t) for t in self.w2))
+        out.keep_ids = keep_ids
+        return out
 
     STAGES = ("route_quantize", "gate_up", "down", "combine", "reap")
 

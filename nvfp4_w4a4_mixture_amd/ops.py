@@ -17,6 +17,7 @@ from ._lib import MoEError, check, lib  # noqa: F401
 
 __all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
            "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
+           "reap_prune_select", "moe_gather_experts",
            "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
 
 
@@ -271,4 +272,31 @@ def reap_saliency(pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids, T: int, 
     st = lib().reap_saliency(_p(pair_sqnorm), _p(topk_w), _p(expert_offsets), _p(sorted_pair_ids), T, k, E,
                              _p(out), _stream(stream))
     check(st, "reap_saliency")
+    return out
+
+
+def reap_prune_select(saliency: torch.Tensor, n_keep: int, out=None, stream=None) -> torch.Tensor:
+    """INT32 ids of the n_keep highest-saliency experts, ascending."""
+    _need(saliency, "saliency", torch.float32)
+    E = saliency.shape[0]
+    if out is None:
+        out = torch.empty((n_keep,), dtype=torch.int32, device=saliency.device)
+    _need(out, "keep_ids", torch.int32, (n_keep,))
+    st = lib().reap_prune_select(_p(saliency), E, n_keep, _p(out), _stream(stream))
+    check(st, "reap_prune_select")
+    return out
+
+
+def moe_gather_experts(src: torch.Tensor, keep_ids: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """out[i] = src[keep_ids[i]] for a per-expert tensor src [E, ...] (any dtype)."""
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    _need(keep_ids, "keep_ids", torch.int32)
+    n = keep_ids.shape[0]
+    if out is None:
+        out = torch.empty((n, *src.shape[1:]), dtype=src.dtype, device=src.device)
+    _need(out, "out", src.dtype, (n, *src.shape[1:]))
+    per = src[0].numel() * src.element_size() if src.shape[0] > 0 else 0
+    st = lib().moe_gather_experts(_p(src), src.shape[0], per, _p(keep_ids), n, _p(out), _stream(stream))
+    check(st, "moe_gather_experts")
     return out

@@ -163,6 +163,28 @@ def test_combine_and_reap_validation(L):
     assert r(P, P, P, P, 4, 2, 300, P, None) == SHAPE
 
 
+def test_prune_validation(L):
+    s = L.reap_prune_select
+    assert s(P, 128, 80, None, None) == NULL
+    assert s(None, 128, 80, P, None) == NULL
+    assert s(P, 128, 0, P, None) == SHAPE
+    assert s(P, 128, 129, P, None) == SHAPE
+    assert s(P, 300, 80, P, None) == SHAPE
+    assert s(P, 128, 80, ctypes.c_void_p(0x10002), None) == ALIGN
+    g = L.moe_gather_experts
+    assert g(None, 128, 64, P, 80, P2, None) == NULL
+    assert g(P, 128, 64, None, 80, P2, None) == NULL
+    assert g(P, 0, 64, P, 80, P2, None) == SHAPE
+    assert g(P, 128, 0, P, 80, P2, None) == SHAPE
+    assert g(P, 128, 64, P, 0, P2, None) == SHAPE
+    assert g(P, 128, 64, P, 70000, P2, None) == SHAPE
+    assert g(P, 1 << 40, 1 << 40, P, 80, P2, None) == SHAPE  # size overflows
+    assert g(P, 128, 64, ctypes.c_void_p(0x30002), 80, P2, None) == ALIGN
+    # src [0x10000, 0x12000) overlaps dst [0x11000, ...)
+    assert g(P, 128, 64, ctypes.c_void_p(0x40000), 80, ctypes.c_void_p(0x11000), None) == SHAPE
+    assert "overlap" in L.moe_last_error().decode()
+
+
 def test_missing_library_fails_loudly(tmp_path):
     from nvfp4_w4a4_mixture_amd import _lib
 

@@ -24,6 +24,7 @@ import torch
 from gpu_cases import bf16_round, check_routing, rel_l2, say, to_np, untile_weight_scales
 from oracle import moe as omoe
 from oracle import nvfp4 as onv
+from oracle import reap as oreap
 from oracle import routing as oroute
 from workloads import CONFIGS, gen
 
@@ -136,3 +137,36 @@ def test_full_size_workload(ci):
     torch.cuda.synchronize()
     err16 = rel_l2(out16.y[tok_d].float().cpu().numpy(), bf16_round(ref_tok["y"]))
     assert err16 <= 2e-3
+    if ci == 3:
+        _pruned_outlier_layer(cfg, layer, xb, x, wr, bias, gs_x, gs_h)
+
+
+def _pruned_outlier_layer(cfg, layer, xb, x, wr, bias, gs_x, gs_h):
+    """The 128-expert layer pruned to 80 (the REAP one-shot step) with a seeded
+    saliency vector given to both sides: kept ids bitwise, the pruned layer's
+    routing on all tokens bitwise, y on sampled tokens rel-L2 <= 2e-3."""
+    n_keep = 80
+    sal = np.random.default_rng(128).random(cfg.E).astype(np.float32)
+    say(f"  pruned layer {cfg.E} -> {n_keep} experts")
+    pl = layer.prune(torch.from_numpy(sal).cuda(), n_keep)
+    out = pl(x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    keep = oreap.keep_ids(sal, n_keep)
+    assert np.array_equal(to_np(pl.keep_ids), keep)
+    wr_k, b_k = oreap.slice_router(wr, bias, keep)
+    ids_ref, _, w64_ref, gap = oroute.route(xb, wr_k, b_k, cfg.k, cfg.rsf)
+    ids = to_np(out.route.topk_ids)
+    near = check_routing(ids, to_np(out.route.topk_w), {"ids": ids_ref, "weights64": w64_ref, "gap": gap}, cfg.rsf,
+                         n_keep)
+    counts, offsets, perm = oroute.permute(ids, n_keep)
+    assert np.array_equal(to_np(out.route.sorted_pair_ids), perm)
+    rng = np.random.default_rng(3)
+    tok = [int(t) for t in rng.choice(cfg.T, 2, replace=False)]
+    need = set(int(keep[e]) for e in ids[tok].reshape(-1))
+    experts = _ptq(cfg.weights, need)
+    ref = omoe.moe_layer(xb, wr_k, b_k, cfg.k, cfg.rsf, gs_x, lambda e: experts[int(keep[e])], gs_h[keep],
+                         tokens=tok)
+    err = rel_l2(to_np(out.y[torch.tensor(tok, device="cuda")]), ref["y"])
+    print(f"  pruned: near-tie tokens {near}, touched {np.count_nonzero(counts)}, y rel-L2 on {tok}: {err:.3e}",
+          flush=True)
+    assert err <= 2e-3
