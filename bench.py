@@ -49,6 +49,10 @@ def parse_args(argv=None):
                     help="REAP one-shot pruning study on --config (3 = the 128-expert layer): saliency from one "
                          "pass, prune to N_KEEP experts, output drift against the unpruned layer for the REAP, a "
                          "seeded random, the lowest-saliency and the most-routed choice, prune time and step times (one JSON line)")
+    ap.add_argument("--shared", action="store_true",
+                    help="BF16 shared expert and block output study on --config: the shared expert alone against "
+                         "its roofline, and the step time of the routed layer, of the block with the shared expert "
+                         "on its own stream, and of the block run serially (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) to calibrate HBM counters")
     return ap.parse_args(argv)
@@ -195,6 +199,64 @@ def reap_prune_study(cfg, layer, x, n_keep: int, steps: int, warmup: int) -> dic
             "steps": steps, "warmup": warmup}
 
 
+def shared_study(cfg, layer, x, steps: int, warmup: int) -> dict:
+    """The BF16 shared expert beside the routed path: its own roofline and what it adds to a step."""
+    import torch
+
+    from nvfp4_w4a4_mixture_amd import ops, workload_io
+
+    w13, w2 = workload_io.shared_expert(cfg.weights, x.device)
+    layer.set_shared_expert(w13, w2)
+    T, H, I = x.shape[0], cfg.H, cfg.I
+    out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    ws = torch.empty((max(ops.moe_shared_workspace_bytes(T, H, I), 1),), dtype=torch.uint8, device=x.device)
+    for _ in range(warmup):
+        ops.moe_shared_expert(x, w13, w2, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ops.moe_shared_expert(x, w13, w2, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_shared = e0.elapsed_time(e1) / steps
+    wbytes = 3 * I * H * 2
+    flops = 2 * T * H * I * 3
+    if cfg.bound == "mfma":
+        achieved = flops / (ms_shared / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "dtype": "bf16"}
+    else:
+        nbytes = wbytes + T * H * 2 + T * H * 4
+        achieved = nbytes / (ms_shared / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+
+    def step_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    def serial():
+        ops.moe_shared_expert(x, w13, w2, out=out, workspace=ws)
+        o = layer(x, out_dtype=torch.bfloat16, reap=False)
+        ops.moe_combine_block(o.pair_out, out, T, cfg.k, torch.bfloat16, y=o.y)
+
+    ms_routed = step_ms(lambda: layer(x, out_dtype=torch.bfloat16, reap=False))
+    ms_block = step_ms(lambda: layer(x, out_dtype=torch.bfloat16, reap=False, block=True))
+    ms_serial = step_ms(serial)
+    return {"study": "shared expert and block output", "workload": cfg.name, "tokens": T, "hidden": H,
+            "shared_intermediate": I, "shared_ms": ms_shared, "shared_weight_bytes": wbytes, "shared_flops": flops,
+            "shared_roofline": roof, "step_ms_routed": ms_routed, "step_ms_block_two_streams": ms_block,
+            "step_ms_block_serial": ms_serial, "tokens_per_s_block": T / ms_block * 1e3,
+            "steps": steps, "warmup": warmup}
+
+
 def cpu_baseline(cfg, n_tokens: int) -> dict:
     """The oracle on a bounded sample of the same workload (the first n_tokens tokens)."""
     import numpy as np
@@ -270,6 +332,9 @@ def main(argv=None) -> int:
     stages = layer.STAGES
     if args.union_sweep:
         print(json.dumps(union_sweep(cfg, layer, x, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.shared:
+        print(json.dumps(shared_study(cfg, layer, x, args.steps, args.warmup)), flush=True)
         return 0
     if args.reap_prune:
         print(json.dumps(reap_prune_study(cfg, layer, x, args.reap_prune, args.steps, args.warmup)), flush=True)

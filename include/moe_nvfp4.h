@@ -251,6 +251,43 @@ moe_status reap_prune_select(const float* saliency, int64_t E, int64_t n_keep, i
 moe_status moe_gather_experts(const void* src, int64_t E_src, int64_t bytes_per_expert,
                               const int32_t* keep_ids, int64_t n_keep, void* dst, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* BF16 shared expert and the MoE block output.  "K-EXAONE-152B-A23B-REAP-
+ * 80E-NVFP4" model card, "Quantization Setup": the shared experts are kept in
+ * BF16 (only the routed experts are NVFP4); "K-EXAONE-152B-A23B-REAP-80E-BF16"
+ * model card, "Pruning Setup": the shared expert is kept whole.  Every token
+ * passes through it, with no routing weight:
+ *
+ *   g = x . W_gate^T, u = x . W_up^T      (BF16 products, FP32 accumulation)
+ *   h = bf16_rne(silu(g) * u)             (the input of the BF16 down Linear)
+ *   shared_out = h . W_down^T             (FP32, [T, H])
+ *   block y[t] = sum_j pair_out[t*k + j] + shared_out[t]
+ *
+ * x [T, H] BF16 with row stride ldx (ldx >= H, ldx % 8 == 0); w13 [2I, H]
+ * BF16, gate rows 0..I-1 then up rows I..2I-1; w2 [H, I] BF16; h [T, I] BF16.
+ * Requires H % 256 == 0, I % 128 == 0, and x, h and each weight matrix under
+ * 4 GiB.  x, w13, w2, h and shared_out must be 16-byte aligned; workspace
+ * 256-byte aligned, of moe_shared_workspace_bytes(T, H, I) bytes (the stage
+ * calls need less; the same size serves them).  For T <= 16 the K dimension
+ * is split across workgroups and the FP32 partial sums are added in a fixed
+ * order, so results are deterministic for every T. */
+size_t moe_shared_workspace_bytes(int64_t T, int64_t H, int64_t I);
+moe_status moe_shared_expert(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
+                             const uint16_t* w13_bf16, const uint16_t* w2_bf16, int64_t I,
+                             float* shared_out, void* workspace, size_t workspace_bytes, void* stream);
+/* The two stages of moe_shared_expert, with h in caller memory. */
+moe_status moe_shared_gate_up(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx,
+                              const uint16_t* w13_bf16, int64_t I, uint16_t* h_bf16, void* workspace,
+                              size_t workspace_bytes, void* stream);
+moe_status moe_shared_down(const uint16_t* h_bf16, int64_t T, int64_t I, const uint16_t* w2_bf16,
+                           int64_t H, float* shared_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+/* moe_combine with the shared expert's row added after the k routed rows:
+ * y[t] = (sum_j pair_out[t*k + j]) + shared_out[t], FP32, then written as in
+ * moe_combine.  shared_out [T, H] FP32, 16-byte aligned. */
+moe_status moe_combine_block(const float* pair_out, const float* shared_out, int64_t T, int64_t k,
+                             int64_t H, int32_t out_dtype, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,11 @@ SIGNATURES = {
     "reap_saliency": (_i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p]),
     "reap_prune_select": (_i32, [_p, _i64, _i64, _p, _p]),
     "moe_gather_experts": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
+    "moe_shared_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "moe_shared_expert": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _sz, _p]),
+    "moe_shared_gate_up": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
+    "moe_shared_down": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
+    "moe_combine_block": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p]),
 }
 
 

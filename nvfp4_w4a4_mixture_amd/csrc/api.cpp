@@ -352,7 +352,7 @@ moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, i
   if (!pair_out || !y) return fail(MOE_ERR_NULL, "moe_combine: a required pointer is NULL");
   if (!aligned(pair_out, 16) || !aligned(y, 16)) return fail(MOE_ERR_ALIGN, "moe_combine: 16-byte alignment required");
   if (moe_status s = check_device()) return s;
-  return launched(moe::launch_combine(pair_out, T, k, H, out_dtype, y, (hipStream_t)stream), "moe_combine");
+  return launched(moe::launch_combine(pair_out, nullptr, T, k, H, out_dtype, y, (hipStream_t)stream), "moe_combine");
 }
 
 moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w, const int32_t* expert_offsets,
@@ -393,6 +393,106 @@ moe_status moe_gather_experts(const void* src, int64_t E_src, int64_t bytes_per_
   if (moe_status s = check_device()) return s;
   return launched(moe::launch_gather_blocks(src, E_src, bytes_per_expert, keep_ids, n_keep, dst, (hipStream_t)stream),
                   "moe_gather_experts");
+}
+
+// ---- BF16 shared expert and the block output
+
+size_t moe_shared_workspace_bytes(int64_t T, int64_t H, int64_t I) {
+  if (T < 0 || H < 1 || I < 1) return 0;
+  return round_up((size_t)T * (size_t)I * 2, 256) + round_up(moe::shared_part_bytes(T, H, I), 256);
+}
+
+namespace {
+
+constexpr uint64_t kOffsetLimit = (uint64_t)1 << 32;  // kernels address each operand with 32-bit byte offsets
+
+moe_status check_shared(const char* fn, int64_t T, int64_t H, int64_t I) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "%s: T must be >= 0", fn);
+  if (H <= 0 || H % 256 != 0) return fail(MOE_ERR_SHAPE, "%s: H must be a positive multiple of 256", fn);
+  if (I <= 0 || I % 128 != 0) return fail(MOE_ERR_SHAPE, "%s: I must be a positive multiple of 128", fn);
+  if ((uint64_t)(2 * I) * (uint64_t)H * 2 >= kOffsetLimit)
+    return fail(MOE_ERR_SHAPE, "%s: each weight matrix must be under 4 GiB", fn);
+  return MOE_OK;
+}
+
+moe_status shared_ws(const char* fn, int64_t T, int64_t H, int64_t I, void* workspace, size_t workspace_bytes,
+                     float** part) {
+  const size_t need = round_up(moe::shared_part_bytes(T, H, I), 256);
+  *part = nullptr;
+  if (need == 0) return MOE_OK;
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  *part = reinterpret_cast<float*>(workspace);
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_shared_gate_up(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx, const uint16_t* w13_bf16,
+                              int64_t I, uint16_t* h_bf16, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_shared_gate_up";
+  if (moe_status s = check_shared(fn, T, H, I)) return s;
+  if (ldx < H || ldx % 8 != 0) return fail(MOE_ERR_SHAPE, "%s: ldx must be >= H and a multiple of 8", fn);
+  if (T == 0) return MOE_OK;
+  if ((uint64_t)T * (uint64_t)ldx * 2 >= kOffsetLimit || (uint64_t)T * (uint64_t)I * 2 >= kOffsetLimit)
+    return fail(MOE_ERR_SHAPE, "%s: x and h must each be under 4 GiB", fn);
+  if (!x_bf16 || !w13_bf16 || !h_bf16) return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(x_bf16, 16) || !aligned(w13_bf16, 16) || !aligned(h_bf16, 16))
+    return fail(MOE_ERR_ALIGN, "%s: x, w13 and h must be 16-byte aligned", fn);
+  float* part;
+  if (moe_status s = shared_ws(fn, T, H, I, workspace, workspace_bytes, &part)) return s;
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_shared_stage(0, x_bf16, ldx, w13_bf16, T, H, I, h_bf16, nullptr, part,
+                                           (hipStream_t)stream), fn);
+}
+
+moe_status moe_shared_down(const uint16_t* h_bf16, int64_t T, int64_t I, const uint16_t* w2_bf16, int64_t H,
+                           float* shared_out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_shared_down";
+  if (moe_status s = check_shared(fn, T, H, I)) return s;
+  if (T == 0) return MOE_OK;
+  if ((uint64_t)T * (uint64_t)I * 2 >= kOffsetLimit) return fail(MOE_ERR_SHAPE, "%s: h must be under 4 GiB", fn);
+  if (!h_bf16 || !w2_bf16 || !shared_out) return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(h_bf16, 16) || !aligned(w2_bf16, 16) || !aligned(shared_out, 16))
+    return fail(MOE_ERR_ALIGN, "%s: h, w2 and shared_out must be 16-byte aligned", fn);
+  float* part;
+  if (moe_status s = shared_ws(fn, T, H, I, workspace, workspace_bytes, &part)) return s;
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_shared_stage(1, h_bf16, I, w2_bf16, T, H, I, nullptr, shared_out, part,
+                                           (hipStream_t)stream), fn);
+}
+
+moe_status moe_shared_expert(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t ldx, const uint16_t* w13_bf16,
+                             const uint16_t* w2_bf16, int64_t I, float* shared_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_shared_expert";
+  if (moe_status s = check_shared(fn, T, H, I)) return s;
+  if (ldx < H || ldx % 8 != 0) return fail(MOE_ERR_SHAPE, "%s: ldx must be >= H and a multiple of 8", fn);
+  if (T == 0) return MOE_OK;
+  const size_t hbytes = round_up((size_t)T * (size_t)I * 2, 256);
+  const size_t need = moe_shared_workspace_bytes(T, H, I);
+  if (!workspace || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn, need);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  uint16_t* h = reinterpret_cast<uint16_t*>(workspace);
+  void* rest = static_cast<unsigned char*>(workspace) + hbytes;
+  if (moe_status s = moe_shared_gate_up(x_bf16, T, H, ldx, w13_bf16, I, h, rest, workspace_bytes - hbytes, stream))
+    return s;
+  return moe_shared_down(h, T, I, w2_bf16, H, shared_out, rest, workspace_bytes - hbytes, stream);
+}
+
+moe_status moe_combine_block(const float* pair_out, const float* shared_out, int64_t T, int64_t k, int64_t H,
+                             int32_t out_dtype, void* y, void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))
+    return fail(MOE_ERR_SHAPE, "moe_combine_block: need T >= 0, k >= 1, H a positive multiple of 4, out_dtype 0 or 1");
+  if (T == 0) return MOE_OK;
+  if (!pair_out || !shared_out || !y) return fail(MOE_ERR_NULL, "moe_combine_block: a required pointer is NULL");
+  if (!aligned(pair_out, 16) || !aligned(shared_out, 16) || !aligned(y, 16))
+    return fail(MOE_ERR_ALIGN, "moe_combine_block: 16-byte alignment required");
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_combine(pair_out, shared_out, T, k, H, out_dtype, y, (hipStream_t)stream),
+                  "moe_combine_block");
 }
 
 }  // extern "C"

@@ -2,8 +2,9 @@
 //
 // combine ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card, "Pruning Setup":
 // renormalized sigmoid routing weights): y[t] = sum_j pair_out[t*k + j], in
-// j order, where pair_out already carries w_{t,j}.  HBM-bound: one float4 of
-// y per thread, k float4 reads.
+// j order, where pair_out already carries w_{t,j}; for the block output the
+// shared expert's FP32 row is added last.  HBM-bound: one float4 of y per
+// thread, k (+1) float4 reads.
 //
 // REAP saliency (same card and section: mean(topk_weight * ||f_e(x)||_2) over
 // routed tokens, routing weights including routed_scaling_factor): one
@@ -15,7 +16,8 @@
 namespace moe {
 
 template <bool BF16_OUT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ pair_out, int64_t T, int k, int64_t H,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ pair_out,
+                                                      const float* __restrict__ add, int64_t T, int k, int64_t H,
                                                       void* __restrict__ y) {
   const int64_t h4 = H / 4;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -25,6 +27,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float4 s = src[0];
   for (int j = 1; j < k; ++j) {
     const float4 v = src[(int64_t)j * h4];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  if (add != nullptr) {  // the block output: routed combine, then the shared expert
+    const float4 v = reinterpret_cast<const float4*>(add)[i];
     s.x += v.x;
     s.y += v.y;
     s.z += v.z;
@@ -64,15 +73,15 @@ __global__ __launch_bounds__(256) void reap_kernel(const float* __restrict__ sq,
   if (threadIdx.x == 0) saliency[e] = n > 0 ? (float)(red[0] / (double)n) : 0.0f;
 }
 
-hipError_t launch_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
-                          hipStream_t st) {
+hipError_t launch_combine(const float* pair_out, const float* add, int64_t T, int64_t k, int64_t H, int out_dtype,
+                          void* y, hipStream_t st) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
   const unsigned grid = (unsigned)((n + 255) / 256);
   if (out_dtype == 0)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, pair_out, T, (int)k, H, y);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, st, pair_out, add, T, (int)k, H, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, pair_out, T, (int)k, H, y);
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, st, pair_out, add, T, (int)k, H, y);
   return hipGetLastError();
 }
 

@@ -57,12 +57,19 @@ int ffn_tiled_bn();
 hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool build_schedule, hipStream_t st);
 hipError_t launch_sq_reduce(const float* part, int64_t npairs, int n_part, float* out, hipStream_t st);
 
-hipError_t launch_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
-                          hipStream_t st);
+// y = sum_j pair_out[t*k + j] (+ add[t] if add != null)
+hipError_t launch_combine(const float* pair_out, const float* add, int64_t T, int64_t k, int64_t H, int out_dtype,
+                          void* y, hipStream_t st);
 hipError_t launch_reap(const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                        int64_t E, float* saliency, hipStream_t st);
 hipError_t launch_prune_select(const float* saliency, int64_t E, int64_t n_keep, int32_t* keep_ids, hipStream_t st);
 hipError_t launch_gather_blocks(const void* src, int64_t n_src, int64_t bytes, const int32_t* ids, int64_t n_ids,
                                 void* dst, hipStream_t st);
+
+// BF16 shared expert: mode 0 = gate_up (a = x, writes h), 1 = down (a = h, writes out)
+bool shared_use_small(int64_t T);
+size_t shared_part_bytes(int64_t T, int64_t H, int64_t I);
+hipError_t launch_shared_stage(int mode, const uint16_t* a, int64_t lda, const uint16_t* w, int64_t T, int64_t H,
+                               int64_t I, uint16_t* h, float* out, float* part, hipStream_t st);
 
 }  // namespace moe

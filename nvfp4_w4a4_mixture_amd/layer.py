@@ -2,6 +2,7 @@
 
 forward(x):  moe_route_quantize -> moe_nvfp4_gate_up_swiglu ->
              moe_nvfp4_down_scatter -> moe_combine (-> reap_saliency)
+block output: moe_shared_expert on a second stream, joined by moe_combine_block
 (the two FFN calls are the stages of moe_nvfp4_grouped_ffn)
 All buffers for a given token count are allocated once and reused, so a
 forward pass enqueues only kernels on the current stream.
@@ -26,6 +27,7 @@ class LayerOut:
     pair_out: torch.Tensor
     pair_sqnorm: Optional[torch.Tensor]
     saliency: Optional[torch.Tensor]
+    shared_out: Optional[torch.Tensor] = None  # the shared expert's FP32 output (block=True)
 
 
 class NVFP4MoELayer:
@@ -44,6 +46,12 @@ class NVFP4MoELayer:
         self.device = w13_codes.device
         self._bufs: dict = {}
         self.keep_ids = None  # set on a layer made by prune(): its experts' ids in the unpruned layer
+        self.shared = None  # (w13 [2I_s, H], w2 [H, I_s]) BF16 of the shared expert, if attached
+        self._side = None  # stream the shared expert runs on, beside the routed path
+
+    def set_shared_expert(self, w13_bf16: torch.Tensor, w2_bf16: torch.Tensor) -> None:
+        """Attach the BF16 shared expert (gate rows then up rows in w13); forward(block=True) adds it."""
+        self.shared = (w13_bf16, w2_bf16)
 
     @classmethod
     def from_bf16(cls, w_router_bf16, bias, k, rsf, x_gs, h_gs, w13_bf16, w2_bf16):
@@ -57,8 +65,8 @@ class NVFP4MoELayer:
         return cls(w_router_bf16, bias, k, rsf, x_gs, h_gs, c13.view(E, 2 * I, H // 2),
                    s13.view(E, 2 * I // 16, H // 128, 16, 8), g13.view(E, 2), c2, s2, g2)
 
-    def _buffers(self, T: int, reap: bool, out_dtype: torch.dtype):
-        key = (T, reap, out_dtype)
+    def _buffers(self, T: int, reap: bool, out_dtype: torch.dtype, block: bool = False):
+        key = (T, reap, out_dtype, block)
         b = self._bufs.get(key)
         if b is None:
             d, E, H, I, k = self.device, self.E, self.H, self.I, self.k
@@ -80,6 +88,13 @@ class NVFP4MoELayer:
                 y=torch.empty((T, H), dtype=out_dtype, device=d),
                 saliency=torch.empty((E,), dtype=torch.float32, device=d) if reap else None,
             )
+            if block:
+                Is = self.shared[1].shape[1]
+                b["shared_out"] = torch.empty((T, H), dtype=torch.float32, device=d)
+                b["shared_ws"] = torch.empty((max(ops.moe_shared_workspace_bytes(T, H, Is), 1),), dtype=torch.uint8,
+                                             device=d)
+                b["ev_in"] = torch.cuda.Event()
+                b["ev_shared"] = torch.cuda.Event()
             self._bufs[key] = b
         return b
 
@@ -98,17 +113,33 @@ class NVFP4MoELayer:
         out = NVFP4MoELayer(g(self.w_router), g(self.bias), self.k, self.rsf, self.x_gs, g(self.h_gs),
                             *(g(t) for t in self.w13), *(g(t) for t in self.w2))
         out.keep_ids = keep_ids
+        out.shared = self.shared  # the shared expert is kept whole
         return out
 
     STAGES = ("route_quantize", "gate_up", "down", "combine", "reap")
 
     def forward(self, x_bf16: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, reap: bool = False,
-                events: Optional[list] = None) -> LayerOut:
+                events: Optional[list] = None, block: bool = False) -> LayerOut:
         """One layer pass.  If `events` is a list of len(STAGES) + 1 timing events,
-        they are recorded on the current stream around each stage."""
+        they are recorded on the current stream around each stage.
+
+        block=True returns the MoE block output (routed combine + shared expert):
+        the shared expert runs on a second stream (default priority) while the
+        routed path runs on the current one, and the combine waits for both."""
         T = x_bf16.shape[0]
-        b = self._buffers(T, reap, out_dtype)
+        if block and self.shared is None:
+            raise ValueError("block=True needs a shared expert (set_shared_expert)")
+        b = self._buffers(T, reap, out_dtype, block)
         mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        if block:
+            cur = torch.cuda.current_stream(self.device)
+            if self._side is None:
+                self._side = torch.cuda.Stream(self.device)
+            b["ev_in"].record(cur)
+            self._side.wait_event(b["ev_in"])
+            ops.moe_shared_expert(x_bf16, *self.shared, out=b["shared_out"], workspace=b["shared_ws"],
+                                  stream=self._side)
+            b["ev_shared"].record(self._side)
         mark(0)
         # routing and the NVFP4 quantization of x in one pass over x
         r, _, _ = ops.moe_route_quantize(x_bf16, self.w_router, self.bias, self.k, self.rsf, self.x_gs,
@@ -124,13 +155,18 @@ class NVFP4MoELayer:
                                    r.sorted_pair_ids, r.topk_w, pair_out=b["pair_out"],
                                    pair_sqnorm=b["pair_sqnorm"] if reap else None, workspace=b["ffn_ws"])
         mark(3)
-        ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
+        if block:
+            torch.cuda.current_stream(self.device).wait_event(b["ev_shared"])
+            ops.moe_combine_block(b["pair_out"], b["shared_out"], T, self.k, out_dtype, y=b["y"])
+        else:
+            ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
         mark(4)
         sal = None
         if reap:
             sal = ops.reap_saliency(b["pair_sqnorm"], r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, self.k,
                                     self.E, out=b["saliency"])
         mark(5)
-        return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal)
+        return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal,
+                        b.get("shared_out"))
 
     __call__ = forward

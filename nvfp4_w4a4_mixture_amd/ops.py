@@ -17,7 +17,8 @@ from ._lib import MoEError, check, lib  # noqa: F401
 
 __all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
            "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
-           "reap_prune_select", "moe_gather_experts",
+           "reap_prune_select", "moe_gather_experts", "moe_shared_workspace_bytes", "moe_shared_expert",
+           "moe_shared_gate_up", "moe_shared_down", "moe_combine_block",
            "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
 
 
@@ -300,3 +301,80 @@ def moe_gather_experts(src: torch.Tensor, keep_ids: torch.Tensor, out=None, stre
     st = lib().moe_gather_experts(_p(src), src.shape[0], per, _p(keep_ids), n, _p(out), _stream(stream))
     check(st, "moe_gather_experts")
     return out
+
+
+def moe_shared_workspace_bytes(T: int, H: int, I: int) -> int:
+    return int(lib().moe_shared_workspace_bytes(T, H, I))
+
+
+def _shared_dims(x_bf16, w13_bf16, w2_bf16):
+    if x_bf16.dim() != 2 or x_bf16.stride(1) != 1:
+        raise ValueError("x_bf16 must be [T, H] with unit column stride")
+    T, H = x_bf16.shape
+    _need(w13_bf16, "w13_bf16", torch.bfloat16)
+    I = w13_bf16.shape[0] // 2
+    _need(w13_bf16, "w13_bf16", torch.bfloat16, (2 * I, H))
+    _need(w2_bf16, "w2_bf16", torch.bfloat16, (H, I))
+    return T, H, I
+
+
+def moe_shared_expert(x_bf16, w13_bf16, w2_bf16, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """BF16 shared expert: FP32 [T, H] = bf16(silu(x Wg^T) * (x Wu^T)) . Wd^T."""
+    _need(x_bf16, "x_bf16", torch.bfloat16, contiguous=False)
+    T, H, I = _shared_dims(x_bf16, w13_bf16, w2_bf16)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x_bf16.device)
+    _need(out, "shared_out", torch.float32, (T, H))
+    nb = moe_shared_workspace_bytes(T, H, I)
+    ws = _workspace(nb, x_bf16.device, workspace)
+    st = lib().moe_shared_expert(_p(x_bf16), T, H, x_bf16.stride(0), _p(w13_bf16), _p(w2_bf16), I, _p(out), _p(ws),
+                                 ws.numel(), _stream(stream))
+    check(st, "moe_shared_expert")
+    return out
+
+
+def moe_shared_gate_up(x_bf16, w13_bf16, h=None, workspace=None, stream=None) -> torch.Tensor:
+    _need(x_bf16, "x_bf16", torch.bfloat16, contiguous=False)
+    if x_bf16.dim() != 2 or x_bf16.stride(1) != 1:
+        raise ValueError("x_bf16 must be [T, H] with unit column stride")
+    T, H = x_bf16.shape
+    _need(w13_bf16, "w13_bf16", torch.bfloat16)
+    I = w13_bf16.shape[0] // 2
+    _need(w13_bf16, "w13_bf16", torch.bfloat16, (2 * I, H))
+    if h is None:
+        h = torch.empty((T, I), dtype=torch.bfloat16, device=x_bf16.device)
+    _need(h, "h_bf16", torch.bfloat16, (T, I))
+    ws = _workspace(moe_shared_workspace_bytes(T, H, I), x_bf16.device, workspace)
+    st = lib().moe_shared_gate_up(_p(x_bf16), T, H, x_bf16.stride(0), _p(w13_bf16), I, _p(h), _p(ws), ws.numel(),
+                                  _stream(stream))
+    check(st, "moe_shared_gate_up")
+    return h
+
+
+def moe_shared_down(h_bf16, w2_bf16, out=None, workspace=None, stream=None) -> torch.Tensor:
+    _need(h_bf16, "h_bf16", torch.bfloat16)
+    T, I = h_bf16.shape
+    _need(w2_bf16, "w2_bf16", torch.bfloat16)
+    H = w2_bf16.shape[0]
+    _need(w2_bf16, "w2_bf16", torch.bfloat16, (H, I))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=h_bf16.device)
+    _need(out, "shared_out", torch.float32, (T, H))
+    ws = _workspace(moe_shared_workspace_bytes(T, H, I), h_bf16.device, workspace)
+    st = lib().moe_shared_down(_p(h_bf16), T, I, _p(w2_bf16), H, _p(out), _p(ws), ws.numel(), _stream(stream))
+    check(st, "moe_shared_down")
+    return out
+
+
+def moe_combine_block(pair_out: torch.Tensor, shared_out: torch.Tensor, T: int, k: int,
+                      out_dtype: torch.dtype = torch.bfloat16, y=None, stream=None) -> torch.Tensor:
+    """y = routed combine + shared expert output."""
+    _need(pair_out, "pair_out", torch.float32)
+    H = pair_out.shape[1]
+    _need(shared_out, "shared_out", torch.float32, (T, H))
+    code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
+    if y is None:
+        y = torch.empty((T, H), dtype=out_dtype, device=pair_out.device)
+    st = lib().moe_combine_block(_p(pair_out), _p(shared_out), T, k, H, code, _p(y), _stream(stream))
+    check(st, "moe_combine_block")
+    return y

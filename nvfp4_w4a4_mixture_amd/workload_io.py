@@ -55,5 +55,11 @@ def build_layer(cfg: LayerConfig, device="cuda", threads: int | None = None,
     return layer, extra
 
 
+def shared_expert(ws: WeightSet, device="cuda") -> tuple[torch.Tensor, torch.Tensor]:
+    """The BF16 shared expert of a weight set: w13 [2I, H] (gate rows, then up rows), w2 [H, I]."""
+    g, u, d = gen.shared_expert_bf16(ws)
+    return bf16_to_device(np.concatenate([g, u], axis=0), device), bf16_to_device(d, device)
+
+
 def tokens(cfg: LayerConfig, device="cuda", T: int | None = None) -> torch.Tensor:
     return bf16_to_device(gen.tokens(cfg, T), device)

@@ -11,6 +11,9 @@ Recipe (per weight set, ``np.random.SeedSequence([0x4E5646, key, stream...])``):
   W_down [H, I] in that order; for the outlier set, each entry is replaced with
   probability 0.005 by a Laplace(0, 0.15) draw; then BF16 round-to-nearest-even;
 * router: W_r [E, H] float32 N(0, 0.02) -> BF16; bias float32 U(-0.1, 0.1);
+* shared expert: float32 N(0, 0.02) draws for W_gate [I, H], W_up [I, H] and
+  W_down [H, I] (intermediate size I of the routed experts, never outliers:
+  it stays BF16), then BF16 round-to-nearest-even;
 * calibration batch: n_cal tokens of N(0, 1) -> BF16;
 * tokens of workload i: N(0, 1) -> BF16, drawn in chunks of 1024 rows, each
   chunk from its own stream so chunks can be drawn in parallel;
@@ -33,7 +36,7 @@ STATIC_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "static")
 X_CHUNK = 1024
 
 # stream ids inside a weight set
-_S_ROUTER_W, _S_ROUTER_B, _S_XCAL, _S_EXPERT = 1, 2, 3, 1000
+_S_ROUTER_W, _S_ROUTER_B, _S_XCAL, _S_SHARED, _S_EXPERT = 1, 2, 3, 4, 1000
 
 
 def _rng(*keys: int) -> np.random.Generator:
@@ -67,6 +70,12 @@ def expert_bf16(ws: WeightSet, e: int):
     u = _weight(rng, (ws.I, ws.H), ws.outliers)
     d = _weight(rng, (ws.H, ws.I), ws.outliers)
     return g, u, d
+
+
+def shared_expert_bf16(ws: WeightSet):
+    """(W_gate [I,H], W_up [I,H], W_down [H,I]) BF16 bit patterns of the shared expert."""
+    rng = _rng(ws.seed_key, _S_SHARED)
+    return tuple(_weight(rng, shape, False) for shape in ((ws.I, ws.H), (ws.I, ws.H), (ws.H, ws.I)))
 
 
 def iter_experts_bf16(ws: WeightSet, experts=None, threads: int | None = None):
