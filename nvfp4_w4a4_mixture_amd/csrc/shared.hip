@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256) void dense_gate_finalize_kernel(const float* _
   if (i >= T * I) return;
   const int64_t t = i / I, c = i - t * I;
   float g = 0.0f, u = 0.0f;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float* p = part + ((int64_t)s * T + t) * 2 * I;
     g += p[c];
@@ -123,6 +124,7 @@ __global__ __launch_bounds__(256) void dense_sum_finalize_kernel(const float* __
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float v = 0.0f;
+#pragma unroll 4
   for (int s = 0; s < S; ++s) v += part[(int64_t)s * n + i];
   out[i] = v;
 }
