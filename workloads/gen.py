@@ -14,6 +14,8 @@ Recipe (per weight set, ``np.random.SeedSequence([0x4E5646, key, stream...])``):
 * shared expert: float32 N(0, 0.02) draws for W_gate [I, H], W_up [I, H] and
   W_down [H, I] (intermediate size I of the routed experts, never outliers:
   it stays BF16), then BF16 round-to-nearest-even;
+* rotation signs (the diagonal of the Hadamard rotation studied on the outlier
+  layer): +-1 with equal probability, one draw per hidden size;
 * calibration batch: n_cal tokens of N(0, 1) -> BF16;
 * tokens of workload i: N(0, 1) -> BF16, drawn in chunks of 1024 rows, each
   chunk from its own stream so chunks can be drawn in parallel;
@@ -37,6 +39,7 @@ X_CHUNK = 1024
 
 # stream ids inside a weight set
 _S_ROUTER_W, _S_ROUTER_B, _S_XCAL, _S_SHARED, _S_EXPERT = 1, 2, 3, 4, 1000
+_ROTATION_KEY = 0x524F54
 
 
 def _rng(*keys: int) -> np.random.Generator:
@@ -76,6 +79,11 @@ def shared_expert_bf16(ws: WeightSet):
     """(W_gate [I,H], W_up [I,H], W_down [H,I]) BF16 bit patterns of the shared expert."""
     rng = _rng(ws.seed_key, _S_SHARED)
     return tuple(_weight(rng, shape, False) for shape in ((ws.I, ws.H), (ws.I, ws.H), (ws.H, ws.I)))
+
+
+def rotation_signs(n: int) -> np.ndarray:
+    """The rotation's diagonal: n float32 signs, +1 or -1 with equal probability (one draw per hidden size)."""
+    return np.where(_rng(_ROTATION_KEY, n).random(n) < 0.5, -1.0, 1.0).astype(np.float32)
 
 
 def iter_experts_bf16(ws: WeightSet, experts=None, threads: int | None = None):
