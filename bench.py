@@ -53,6 +53,9 @@ def parse_args(argv=None):
                     help="BF16 shared expert and block output study on --config: the shared expert alone against "
                          "its roofline, and the step time of the routed layer, of the block with the shared expert "
                          "on its own stream, and of the block run serially (one JSON line)")
+    ap.add_argument("--rotation", action="store_true",
+                    help="offline Hadamard rotation study on --config: time the rotation of every W_gate/W_up row and "
+                         "of the tokens for block sizes 16, 128 and 2048 against the HBM roofline (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) to calibrate HBM counters")
     return ap.parse_args(argv)
@@ -257,6 +260,39 @@ def shared_study(cfg, layer, x, steps: int, warmup: int) -> dict:
             "steps": steps, "warmup": warmup}
 
 
+def rotation_study(cfg, x, steps: int, warmup: int) -> dict:
+    """The offline rotation kernel on the layer's W13 rows and tokens: time and HBM rate per block size."""
+    import torch
+
+    from nvfp4_w4a4_mixture_amd import ops, workload_io
+    from workloads import gen
+
+    ws = cfg.weights
+    w13, _ = workload_io.expert_weights_bf16(ws, x.device)
+    w = w13.view(-1, ws.H)
+    out = torch.empty_like(w)
+    xo = torch.empty_like(x)
+    s = torch.from_numpy(gen.rotation_signs(ws.H)).to(x.device)
+    rows = []
+    for blk in (16, 128, 2048):
+        for name, src, dst in (("w13", w, out), ("tokens", x, xo)):
+            for _ in range(max(1, warmup)):
+                ops.hadamard_rotate_bf16(src, s, blk, out=dst)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = max(1, steps)
+            e0.record()
+            for _ in range(n):
+                ops.hadamard_rotate_bf16(src, s, blk, out=dst)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+            nbytes = 2 * src.numel() * 2  # BF16 read and written once
+            rows.append({"block": blk, "operand": name, "rows": src.shape[0], "cols": src.shape[1], "ms": ms,
+                         "GB_per_s": nbytes / (ms / 1e3) / 1e9, "hbm_frac": nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS})
+    return {"study": "offline Hadamard rotation kernel", "workload": cfg.name, "rows": rows, "steps": steps,
+            "warmup": warmup}
+
+
 def cpu_baseline(cfg, n_tokens: int) -> dict:
     """The oracle on a bounded sample of the same workload (the first n_tokens tokens)."""
     import numpy as np
@@ -332,6 +368,10 @@ def main(argv=None) -> int:
     stages = layer.STAGES
     if args.union_sweep:
         print(json.dumps(union_sweep(cfg, layer, x, args.steps, args.warmup)), flush=True)
+        return 0
+    if args.rotation:
+        del layer
+        print(json.dumps(rotation_study(cfg, x, args.steps, args.warmup)), flush=True)
         return 0
     if args.shared:
         print(json.dumps(shared_study(cfg, layer, x, args.steps, args.warmup)), flush=True)

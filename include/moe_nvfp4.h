@@ -288,6 +288,26 @@ moe_status moe_shared_down(const uint16_t* h_bf16, int64_t T, int64_t I, const u
 moe_status moe_combine_block(const float* pair_out, const float* shared_out, int64_t T, int64_t k,
                              int64_t H, int32_t out_dtype, void* y, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Offline Hadamard rotation of the hidden dimension ("[NetsPresso AQ Deep
+ * Dive] How to Quantize the K-EXAONE-236B Model to 4-Bit (NVFP4)", "Offline
+ * Fusion of Multiple Quantization Algorithms": the weights' coordinates are
+ * rotated before NVFP4 quantization so that outliers do not pile up in one
+ * block; the rotation is absorbed into the weights).  Row by row:
+ *
+ *   dst[r, :] = bf16_rne( (src[r, :] * signs) . blockdiag(H_b, ..., H_b) / sqrt(b) )
+ *
+ * H_b is the +-1 Sylvester Hadamard matrix of size b = block (a power of two,
+ * 2 <= b <= cols, cols % b == 0); signs [cols] FP32 +-1 (NULL = all +1).
+ * Rotating x and each row of W_gate, W_up and the router by the same R keeps
+ * x W^T unchanged in exact arithmetic.  src/dst [rows, cols] BF16 with row
+ * strides ld_src/ld_dst (>= cols, multiples of 8); cols a multiple of 8, at
+ * most 16384; src and dst 16-byte aligned and either identical (in place, same
+ * stride) or not overlapping.  FP32 butterflies in a fixed order. */
+moe_status hadamard_rotate_bf16(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                const float* signs, int64_t block, uint16_t* dst, int64_t ld_dst,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,7 @@ SIGNATURES = {
     "moe_shared_gate_up": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
     "moe_shared_down": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
     "moe_combine_block": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p]),
+    "hadamard_rotate_bf16": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
 }
 
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "lib")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_nvfp4.so"
-SOURCES = ["quantize.hip", "route.hip", "ffn.hip", "combine.hip", "prune.hip", "shared.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "route.hip", "ffn.hip", "combine.hip", "prune.hip", "shared.hip", "rotate.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

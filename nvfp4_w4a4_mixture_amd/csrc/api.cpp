@@ -495,4 +495,31 @@ moe_status moe_combine_block(const float* pair_out, const float* shared_out, int
                   "moe_combine_block");
 }
 
+// ---- offline Hadamard rotation
+
+moe_status hadamard_rotate_bf16(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src, const float* signs,
+                                int64_t block, uint16_t* dst, int64_t ld_dst, void* stream) {
+  const char* fn = "hadamard_rotate_bf16";
+  if (rows < 0 || rows > INT32_MAX) return fail(MOE_ERR_SHAPE, "%s: need 0 <= rows < 2^31", fn);
+  if (cols < 8 || cols % 8 != 0 || cols > moe::hadamard_max_cols())
+    return fail(MOE_ERR_SHAPE, "%s: cols must be a multiple of 8 in [8, %lld]", fn, (long long)moe::hadamard_max_cols());
+  if (block < 2 || (block & (block - 1)) != 0 || block > cols || cols % block != 0)
+    return fail(MOE_ERR_SHAPE, "%s: block must be a power of two >= 2 that divides cols", fn);
+  if (ld_src < cols || ld_dst < cols || ld_src % 8 != 0 || ld_dst % 8 != 0)
+    return fail(MOE_ERR_SHAPE, "%s: leading dimensions must be >= cols and multiples of 8", fn);
+  if (rows == 0) return MOE_OK;
+  if (!src || !dst) return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(signs, 4))
+    return fail(MOE_ERR_ALIGN, "%s: src and dst must be 16-byte aligned, signs 4-byte aligned", fn);
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t s1 = s0 + (uintptr_t)(((rows - 1) * ld_src + cols) * 2);
+  const uintptr_t d1 = d0 + (uintptr_t)(((rows - 1) * ld_dst + cols) * 2);
+  const bool in_place = s0 == d0 && ld_src == ld_dst;
+  if (!in_place && s0 < d1 && d0 < s1)
+    return fail(MOE_ERR_SHAPE, "%s: src and dst overlap (only the exact in-place call is allowed)", fn);
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_hadamard_rotate(src, rows, cols, ld_src, signs, block, dst, ld_dst, (hipStream_t)stream),
+                  fn);
+}
+
 }  // extern "C"

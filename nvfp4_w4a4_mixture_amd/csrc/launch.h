@@ -72,4 +72,9 @@ size_t shared_part_bytes(int64_t T, int64_t H, int64_t I);
 hipError_t launch_shared_stage(int mode, const uint16_t* a, int64_t lda, const uint16_t* w, int64_t T, int64_t H,
                                int64_t I, uint16_t* h, float* out, float* part, hipStream_t st);
 
+// dst = bf16((src * signs) . blockdiag(H_b) / sqrt(b)), row by row
+int64_t hadamard_max_cols();
+hipError_t launch_hadamard_rotate(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src, const float* signs,
+                                  int64_t b, uint16_t* dst, int64_t ld_dst, hipStream_t st);
+
 }  // namespace moe

@@ -18,7 +18,7 @@ from ._lib import MoEError, check, lib  # noqa: F401
 __all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
            "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
            "reap_prune_select", "moe_gather_experts", "moe_shared_workspace_bytes", "moe_shared_expert",
-           "moe_shared_gate_up", "moe_shared_down", "moe_combine_block",
+           "moe_shared_gate_up", "moe_shared_down", "moe_combine_block", "hadamard_rotate_bf16",
            "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
 
 
@@ -378,3 +378,25 @@ def moe_combine_block(pair_out: torch.Tensor, shared_out: torch.Tensor, T: int, 
     st = lib().moe_combine_block(_p(pair_out), _p(shared_out), T, k, H, code, _p(y), _stream(stream))
     check(st, "moe_combine_block")
     return y
+
+
+def hadamard_rotate_bf16(src: torch.Tensor, signs: Optional[torch.Tensor], block: int, out=None,
+                         stream=None) -> torch.Tensor:
+    """Rows of src [..., cols] (BF16) times D blockdiag(H_block) / sqrt(block); out may be src (in place)."""
+    _need(src, "src", torch.bfloat16, contiguous=False)
+    if src.stride(-1) != 1:
+        raise ValueError("src must have unit column stride")
+    cols = src.shape[-1]
+    s2 = src.reshape(-1, cols) if src.dim() != 2 else src
+    if out is None:
+        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+    _need(out, "out", torch.bfloat16, tuple(src.shape), contiguous=False)
+    o2 = out.reshape(-1, cols) if out.dim() != 2 else out
+    if o2.data_ptr() != out.data_ptr() or (out.dim() != 2 and not out.is_contiguous()):
+        raise ValueError("out must be 2-D or contiguous")
+    if signs is not None:
+        _need(signs, "signs", torch.float32, (cols,))
+    st = lib().hadamard_rotate_bf16(_p(s2), s2.shape[0], cols, s2.stride(0), _p(signs), block, _p(o2), o2.stride(0),
+                                    _stream(stream))
+    check(st, "hadamard_rotate_bf16")
+    return out

@@ -12,7 +12,8 @@ Two kinds of layer input are not plain random draws:
 Both are computed here with the oracle's own arithmetic on the seeded inputs
 of ``workloads.gen`` and stored as float32 bit patterns, so that every run on
 either side reads identical values.  Run: ``python -m oracle.make_static_inputs
-[set ...]`` with set names from ``workloads.configs.WEIGHT_SETS`` or ``zipf``.
+[set ...]`` with set names from ``workloads.configs.WEIGHT_SETS``, ``zipf`` or
+``rotation`` (gs_x of the Hadamard-rotated calibration batch of the outlier set).
 """
 
 from __future__ import annotations
@@ -26,7 +27,7 @@ import numpy as np
 
 from workloads import CONFIGS, WEIGHT_SETS, gen
 
-from . import moe, routing
+from . import moe, nvfp4, rotation, routing
 
 
 def _bits(a) -> list[str]:
@@ -60,6 +61,25 @@ def calibration(ws_name: str, threads: int) -> None:
     })
 
 
+ROTATION_BLOCKS = (16, 128, 2048)
+
+
+def rotation_calibration(ws_name: str) -> None:
+    """gs_x of the Hadamard-rotated calibration batch, one per rotation block size."""
+    ws = WEIGHT_SETS[ws_name]
+    xc = gen.x_cal(ws)
+    s = gen.rotation_signs(ws.H)
+    out = {}
+    for b in ROTATION_BLOCKS:
+        xr = gen.bf16_bits_to_f32(rotation.rotate_bf16(xc, s, b))
+        out[str(b)] = _bits([nvfp4.global_scale(np.max(np.abs(xr)))])[0]
+    _write(f"rotation_{ws.name}.json", {
+        "what": "static gs_x = 2688/amax of the rotated calibration batch, per rotation block size",
+        "weight_set": ws.name, "n_cal": ws.n_cal, "gs_x_bits": out,
+        "gs_x": {b: float(gen._f32([v])[0]) for b, v in out.items()},
+    })
+
+
 def zipf_bias(cfg_index: int = 2, steps: int = 400) -> None:
     cfg = CONFIGS[cfg_index]
     assert cfg.bias == "zipf"
@@ -89,10 +109,12 @@ def zipf_bias(cfg_index: int = 2, steps: int = 400) -> None:
 
 def main(argv) -> None:
     threads = min(8, len(os.sched_getaffinity(0)))
-    todo = argv or ["tiny8", "e80", "e128_outlier", "zipf"]
+    todo = argv or ["tiny8", "e80", "e128_outlier", "zipf", "rotation"]
     for name in todo:
         if name == "zipf":
             zipf_bias()
+        elif name == "rotation":
+            rotation_calibration("e128_outlier")
         else:
             calibration(name, threads)
 

@@ -20,6 +20,8 @@ Readings (the plainest rotation of that kind):
   W_down's output side, the residual stream, would carry the inverse rotation
   into the next layer and is left as it is;
 * rotated values are rounded once to BF16 (the model's dtype) before the RTN;
+  the float64 value rounded is (sum of the +-1 products) / sqrt(b), whose sum is
+  exact for BF16 inputs of moderate range;
 * the rotated layer calibrates gs_x on the rotated calibration batch and
   reuses gs_h, since h is the same function of x in exact arithmetic.
 
@@ -51,9 +53,9 @@ def rotate_rows(values: np.ndarray, signs: np.ndarray, b: int) -> np.ndarray:
     n = v.shape[-1]
     if n % b:
         raise ValueError("b must divide the row length")
-    hb = sylvester(b) / np.sqrt(b)
     vs = v * np.asarray(signs, dtype=np.float64)
-    return (vs.reshape(*v.shape[:-1], n // b, b) @ hb).reshape(v.shape)
+    # the +-1 products are summed first, then divided once by sqrt(b)
+    return (vs.reshape(*v.shape[:-1], n // b, b) @ sylvester(b)).reshape(v.shape) / np.sqrt(b)
 
 
 def rotate_bf16(bits: np.ndarray, signs: np.ndarray, b: int) -> np.ndarray:

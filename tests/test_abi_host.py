@@ -185,6 +185,35 @@ def test_prune_validation(L):
     assert "overlap" in L.moe_last_error().decode()
 
 
+def test_shared_and_rotation_validation(L):
+    g = L.moe_shared_gate_up
+    assert g(P, 4, 250, 256, P, 128, P, P, 1 << 20, None) == SHAPE  # H % 256
+    assert g(P, 4, 256, 256, P, 100, P, P, 1 << 20, None) == SHAPE  # I % 128
+    assert g(P, 4, 256, 250, P, 128, P, P, 1 << 20, None) == SHAPE  # ldx < H
+    assert g(None, 4, 256, 256, P, 128, P, P, 1 << 20, None) == NULL
+    assert g(ctypes.c_void_p(0x10008), 4, 256, 256, P, 128, P, P, 1 << 20, None) == ALIGN
+    assert g(P, 4, 256, 256, P, 128, P, None, 0, None) == WORKSPACE  # T <= 16 needs the partial sums
+    assert g(P, 0, 256, 256, P, 128, P, None, 0, None) == OK
+    assert L.moe_shared_workspace_bytes(4, 256, 128) >= 4 * 128 * 2 and L.moe_shared_workspace_bytes(-1, 256, 128) == 0
+    d = L.moe_shared_down
+    assert d(P, 4, 128, P, 256, None, P, 1 << 20, None) == NULL
+    assert d(P, 4, 128, P, 256, ctypes.c_void_p(0x10004), P, 1 << 20, None) == ALIGN
+    e = L.moe_shared_expert
+    assert e(P, 4, 256, 256, P, P, 128, P, P, 16, None) == WORKSPACE
+    c = L.moe_combine_block
+    assert c(P, None, 4, 2, 64, 0, P, None) == NULL
+    assert c(P, P, 4, 2, 66, 0, P, None) == SHAPE
+    r = L.hadamard_rotate_bf16
+    assert r(P, 4, 256, 256, None, 48, P2, 256, None) == SHAPE  # block not a power of two
+    assert r(P, 4, 256, 256, None, 512, P2, 256, None) == SHAPE  # block > cols
+    assert r(P, 4, 260, 264, None, 4, P2, 264, None) == SHAPE  # cols % 8
+    assert r(P, 4, 32768, 32768, None, 2, P2, 32768, None) == SHAPE  # cols above the LDS row limit
+    assert r(P, 4, 256, 256, None, 16, None, 256, None) == NULL
+    assert r(P, 4, 256, 256, None, 16, ctypes.c_void_p(0x20008), 256, None) == ALIGN
+    assert r(P, 4, 256, 256, None, 16, ctypes.c_void_p(0x10100), 256, None) == SHAPE  # partial overlap
+    assert r(P, 0, 256, 256, None, 16, P2, 256, None) == OK
+
+
 def test_missing_library_fails_loudly(tmp_path):
     from nvfp4_w4a4_mixture_amd import _lib
 

@@ -176,6 +176,13 @@ def global_scales(ws: WeightSet):
     return np.float32(gs_x), gs_h
 
 
+@lru_cache(maxsize=None)
+def rotated_gs_x(ws: WeightSet, block: int) -> np.float32:
+    """Calibrated gs_x of the Hadamard-rotated calibration batch (rotation block size `block`)."""
+    d = _load_json(f"rotation_{ws.name}.json")
+    return np.float32(_f32([d["gs_x_bits"][str(block)]])[0])
+
+
 def router_bias(cfg: LayerConfig) -> np.ndarray:
     if cfg.bias == "uniform":
         return router_bias_uniform(cfg.weights)
