@@ -120,8 +120,8 @@ class NVFP4MoELayer:
 
     def forward(self, x_bf16: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, reap: bool = False,
                 events: Optional[list] = None, block: bool = False) -> LayerOut:
-        """One layer pass.  If `events` is a list of len(STAGES) + 1 timing events,
-        they are recorded on the current stream around each stage.
+        """One layer pass.  If `events` is a list of len(STAGES) + 1 timing events
+        (entries may be None), they are recorded on the current stream around each stage.
 
         block=True returns the MoE block output (routed combine + shared expert):
         the shared expert runs on a second stream (default priority) while the
@@ -130,7 +130,10 @@ class NVFP4MoELayer:
         if block and self.shared is None:
             raise ValueError("block=True needs a shared expert (set_shared_expert)")
         b = self._buffers(T, reap, out_dtype, block)
-        mark = (lambda i: events[i].record()) if events is not None else (lambda i: None)
+        def mark(i):  # record event i if one was given for that position
+            if events is not None and events[i] is not None:
+                events[i].record()
+
         if block:
             cur = torch.cuda.current_stream(self.device)
             if self._side is None:
