@@ -151,6 +151,21 @@ moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t
                                   uint8_t* codes, uint8_t* scales_e4m3, float* global_scales,
                                   void* stream);
 
+/* One-time prepack of canonical NVFP4 expert weights into the layout the
+ * FFN calls read, and its exact inverse.  Canonical: codes [E, N, K/2] and
+ * scales [E, N, K/16], both row-major (the form nvfp4_quantize_act writes and
+ * an NVFP4 checkpoint stores).  Packed: codes unchanged, scales in the tiled
+ * order of the header comment over the E*N rows.  Bit-preserving, so
+ * unpack(prepack(w)) == w.  kind 0 = w13 (N = 2I rows, K = H), 1 = w2
+ * (N = H, K = I).  Requires N % 16 == 0, K % 128 == 0; scale arrays 8-byte
+ * aligned and not overlapping; the code arrays may be the same (no copy). */
+moe_status moe_nvfp4_prepack_weights(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N,
+                                     int64_t K, int32_t kind, uint8_t* packed_codes,
+                                     uint8_t* packed_scales, void* stream);
+moe_status moe_nvfp4_unpack_weights(const uint8_t* packed_codes, const uint8_t* packed_scales, int64_t E,
+                                    int64_t N, int64_t K, int32_t kind, uint8_t* codes, uint8_t* scales,
+                                    void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* The grouped NVFP4 W4A4 expert FFN ("K-EXAONE-152B-A23B-REAP-80E-NVFP4"
  * model card, "Quantization Setup": every routed expert Linear is W4A4):

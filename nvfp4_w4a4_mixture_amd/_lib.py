@@ -53,6 +53,8 @@ SIGNATURES = {
     "moe_shared_down": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
     "moe_combine_block": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "hadamard_rotate_bf16": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
+    "moe_nvfp4_prepack_weights": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p, _p]),
+    "moe_nvfp4_unpack_weights": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p, _p]),
 }
 
 

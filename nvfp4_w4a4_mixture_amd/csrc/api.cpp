@@ -522,4 +522,42 @@ moe_status hadamard_rotate_bf16(const uint16_t* src, int64_t rows, int64_t cols,
                   fn);
 }
 
+// ---- one-time weight prepack (canonical -> kernel layout) and its inverse
+
+static moe_status relayout_weights(const char* fn, const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N,
+                                   int64_t K, int32_t kind, uint8_t* out_codes, uint8_t* out_scales, bool to_tiled,
+                                   void* stream) {
+  if (kind != 0 && kind != 1) return fail(MOE_ERR_SHAPE, "%s: kind must be 0 (w13) or 1 (w2)", fn);
+  if (E < 0 || N <= 0 || K <= 0 || N % 16 != 0 || K % 128 != 0)
+    return fail(MOE_ERR_SHAPE, "%s: need E >= 0, N a positive multiple of 16, K a positive multiple of 128", fn);
+  if (kind == 0 && N % 2 != 0) return fail(MOE_ERR_SHAPE, "%s: w13 has 2I rows", fn);
+  if (E == 0) return MOE_OK;
+  if (!codes || !scales || !out_codes || !out_scales) return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (!aligned(scales, 8) || !aligned(out_scales, 8)) return fail(MOE_ERR_ALIGN, "%s: scale arrays must be 8-byte aligned", fn);
+  const int64_t rows = E * N;
+  const size_t scale_bytes = (size_t)rows * (size_t)(K / 16);
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(scales), b0 = reinterpret_cast<uintptr_t>(out_scales);
+  if (a0 < b0 + scale_bytes && b0 < a0 + scale_bytes)
+    return fail(MOE_ERR_SHAPE, "%s: the scale arrays must not overlap", fn);
+  if (moe_status s = check_device()) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (out_codes != codes) {
+    const hipError_t e = hipMemcpyAsync(out_codes, codes, (size_t)rows * (size_t)(K / 2), hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return fail(MOE_ERR_LAUNCH, "%s: code copy: %s", fn, hipGetErrorString(e));
+  }
+  return launched(moe::launch_relayout_scales(scales, rows, K, to_tiled, out_scales, st), fn);
+}
+
+moe_status moe_nvfp4_prepack_weights(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N, int64_t K,
+                                     int32_t kind, uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  return relayout_weights("moe_nvfp4_prepack_weights", codes, scales, E, N, K, kind, packed_codes, packed_scales, true,
+                          stream);
+}
+
+moe_status moe_nvfp4_unpack_weights(const uint8_t* packed_codes, const uint8_t* packed_scales, int64_t E, int64_t N,
+                                    int64_t K, int32_t kind, uint8_t* codes, uint8_t* scales, void* stream) {
+  return relayout_weights("moe_nvfp4_unpack_weights", packed_codes, packed_scales, E, N, K, kind, codes, scales, false,
+                          stream);
+}
+
 }  // extern "C"

@@ -37,6 +37,9 @@ struct FfnArgs {
 hipError_t launch_quantize_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, const float* gs,
                                 int64_t rows_per_gs, uint8_t* codes, uint8_t* scales, bool tiled_scales,
                                 hipStream_t stream);
+// canonical [rows, K/16] scales <-> tiled [rows/16, K/128, 16, 8] (rows % 16 == 0, K % 128 == 0)
+hipError_t launch_relayout_scales(const uint8_t* src, int64_t rows, int64_t K, bool to_tiled, uint8_t* dst,
+                                  hipStream_t st);
 hipError_t launch_weight_global_scales(const uint16_t* w, int64_t batch, int64_t per_matrix, float* gs,
                                        hipStream_t stream);
 

@@ -109,3 +109,36 @@ hipError_t launch_weight_global_scales(const uint16_t* w, int64_t batch, int64_t
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// One-time relayout of canonical NVFP4 weight scales ([R, K/16] row-major) into
+// the tiled order the expert kernels read ([R/16, K/128, 16, 8]), and back.
+// Thread t moves the 8 scale bytes of one (row, 128-column group): one 8-byte
+// read and one 8-byte write.  Codes are kept in their canonical layout.
+template <bool TO_TILED>
+__global__ __launch_bounds__(256) void relayout_scales_kernel(const uint8_t* __restrict__ src, int64_t rows,
+                                                              int64_t K, uint8_t* __restrict__ dst) {
+  const int64_t groups = K / 128;  // 8-byte scale groups per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * groups) return;
+  const int64_t r = i / groups, g = i - r * groups;
+  const int64_t canon = r * (K / 16) + 8 * g;
+  const int64_t tiled = tiled_scale_index(r, 8 * g, K);
+  if (TO_TILED)
+    *reinterpret_cast<uint2*>(dst + tiled) = *reinterpret_cast<const uint2*>(src + canon);
+  else
+    *reinterpret_cast<uint2*>(dst + canon) = *reinterpret_cast<const uint2*>(src + tiled);
+}
+
+hipError_t launch_relayout_scales(const uint8_t* src, int64_t rows, int64_t K, bool to_tiled, uint8_t* dst,
+                                  hipStream_t st) {
+  const int64_t n = rows * (K / 128);
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (to_tiled) hipLaunchKernelGGL(relayout_scales_kernel<true>, dim3(grid), dim3(256), 0, st, src, rows, K, dst);
+  else hipLaunchKernelGGL(relayout_scales_kernel<false>, dim3(grid), dim3(256), 0, st, src, rows, K, dst);
+  return hipGetLastError();
+}
+
+}  // namespace moe

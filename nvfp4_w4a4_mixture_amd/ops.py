@@ -19,6 +19,7 @@ __all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quant
            "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
            "reap_prune_select", "moe_gather_experts", "moe_shared_workspace_bytes", "moe_shared_expert",
            "moe_shared_gate_up", "moe_shared_down", "moe_combine_block", "hadamard_rotate_bf16",
+           "moe_nvfp4_prepack_weights", "moe_nvfp4_unpack_weights",
            "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
 
 
@@ -400,3 +401,30 @@ def hadamard_rotate_bf16(src: torch.Tensor, signs: Optional[torch.Tensor], block
                                     _stream(stream))
     check(st, "hadamard_rotate_bf16")
     return out
+
+
+def _relayout(fn: str, codes: torch.Tensor, scales: torch.Tensor, kind: int, to_tiled: bool, stream=None):
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    E, N, kh = codes.shape
+    K = 2 * kh
+    if to_tiled:
+        _need(scales, "scales", torch.uint8, (E, N, K // 16))
+        out_s = torch.empty((E, N // 16, K // 128, 16, 8), dtype=torch.uint8, device=codes.device)
+    else:
+        _need(scales, "scales", torch.uint8, (E, N // 16, K // 128, 16, 8))
+        out_s = torch.empty((E, N, K // 16), dtype=torch.uint8, device=codes.device)
+    out_c = torch.empty_like(codes)
+    st = getattr(lib(), fn)(_p(codes), _p(scales), E, N, K, kind, _p(out_c), _p(out_s), _stream(stream))
+    check(st, fn)
+    return out_c, out_s
+
+
+def moe_nvfp4_prepack_weights(codes: torch.Tensor, scales: torch.Tensor, kind: int, stream=None):
+    """Canonical (codes [E, N, K/2], scales [E, N, K/16]) -> (codes, tiled scales [E, N/16, K/128, 16, 8])."""
+    return _relayout("moe_nvfp4_prepack_weights", codes, scales, kind, True, stream)
+
+
+def moe_nvfp4_unpack_weights(codes: torch.Tensor, packed_scales: torch.Tensor, kind: int, stream=None):
+    """Exact inverse of moe_nvfp4_prepack_weights."""
+    return _relayout("moe_nvfp4_unpack_weights", codes, packed_scales, kind, False, stream)

@@ -214,6 +214,17 @@ def test_shared_and_rotation_validation(L):
     assert r(P, 0, 256, 256, None, 16, P2, 256, None) == OK
 
 
+def test_prepack_validation(L):
+    for fn in (L.moe_nvfp4_prepack_weights, L.moe_nvfp4_unpack_weights):
+        assert fn(P, P, 2, 24, 256, 1, P2, ctypes.c_void_p(0x30000), None) == SHAPE  # N % 16
+        assert fn(P, P, 2, 32, 200, 1, P2, ctypes.c_void_p(0x30000), None) == SHAPE  # K % 128
+        assert fn(P, P, 2, 32, 256, 2, P2, ctypes.c_void_p(0x30000), None) == SHAPE  # kind
+        assert fn(P, None, 2, 32, 256, 1, P2, ctypes.c_void_p(0x30000), None) == NULL
+        assert fn(P, ctypes.c_void_p(0x10004), 2, 32, 256, 1, P2, ctypes.c_void_p(0x30000), None) == ALIGN
+        assert fn(P, P, 2, 32, 256, 1, P2, ctypes.c_void_p(0x10008), None) == SHAPE  # scale arrays overlap
+        assert fn(P, P, 0, 32, 256, 1, P2, ctypes.c_void_p(0x30000), None) == OK
+
+
 def test_missing_library_fails_loudly(tmp_path):
     from nvfp4_w4a4_mixture_amd import _lib
 

@@ -338,3 +338,41 @@ def test_repeat_runs_are_bitwise_identical(ops):
     b = layer(x, out_dtype=torch.float32, reap=True)
     torch.cuda.synchronize()
     assert torch.equal(ya, b.y) and torch.equal(sa, b.saliency) and torch.equal(pa, b.route.sorted_pair_ids)
+
+
+def test_prepack_roundtrip_and_canonical_weights(ops):
+    """unpack(prepack(w)) == w for arbitrary bytes; prepacking the oracle's canonical RTN weights gives the
+    library quantizer's layout bit for bit, and a layer built from them gives the same output."""
+    rng = np.random.default_rng(21)
+    codes = torch.from_numpy(rng.integers(0, 256, (3, 32, 128), dtype=np.uint8)).cuda()
+    scales = torch.from_numpy(rng.integers(0, 256, (3, 32, 16), dtype=np.uint8)).cuda()
+    say("prepack round trip")
+    pc, ps = ops.moe_nvfp4_prepack_weights(codes, scales, 1)
+    uc, us = ops.moe_nvfp4_unpack_weights(pc, ps, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(pc, codes) and torch.equal(uc, codes) and torch.equal(us, scales)
+    assert np.array_equal(untile_weight_scales(to_np(ps)), to_np(scales))
+
+    case = random_case("prepack", 23, 40, 512, 256, 6, 2)
+    layer = gpu_layer(case)
+    q = case.experts_q
+    c13 = np.stack([np.concatenate([e.gate_codes, e.up_codes]) for e in q])
+    s13 = np.stack([np.concatenate([e.gate_scales, e.up_scales]) for e in q])
+    c2 = np.stack([e.down_codes for e in q])
+    s2 = np.stack([e.down_scales for e in q])
+    say("prepack of oracle weights")
+    p13 = ops.moe_nvfp4_prepack_weights(torch.from_numpy(c13).cuda(), torch.from_numpy(s13).cuda(), 0)
+    p2 = ops.moe_nvfp4_prepack_weights(torch.from_numpy(c2).cuda(), torch.from_numpy(s2).cuda(), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(p13[0], layer.w13[0]) and torch.equal(p13[1], layer.w13[1])
+    assert torch.equal(p2[0], layer.w2[0]) and torch.equal(p2[1], layer.w2[1])
+    from nvfp4_w4a4_mixture_amd.layer import NVFP4MoELayer
+    g13 = torch.tensor([[e.gate_gs, e.up_gs] for e in q], dtype=torch.float32, device="cuda")
+    g2 = torch.tensor([e.down_gs for e in q], dtype=torch.float32, device="cuda")
+    other = NVFP4MoELayer(layer.w_router, layer.bias, case.k, case.rsf, layer.x_gs, layer.h_gs, p13[0], p13[1], g13,
+                          p2[0], p2[1], g2)
+    x = dev_bf16(case.x)
+    y0 = layer(x, out_dtype=torch.float32).y.clone()
+    y1 = other(x, out_dtype=torch.float32).y
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
