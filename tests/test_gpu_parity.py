@@ -20,7 +20,7 @@ from gpu_cases import (bf16_round, check_routing, config_case, dev_bf16, gpu_lay
                        oracle_perm, random_case, rel_l2, say, to_np, untile_weight_scales)
 from oracle import nvfp4 as onv
 from oracle import routing as oroute
-from workloads import CONFIGS, gen
+from workloads import CONFIGS, by_name, gen
 
 pytestmark = pytest.mark.gpu
 
@@ -264,7 +264,7 @@ def _layer_check(ops, case, reap=True):
 
 
 def test_layer_parity_config0(ops):
-    _layer_check(ops, config_case(CONFIGS[0]))
+    _layer_check(ops, config_case(by_name("tiny")))
 
 
 @pytest.mark.parametrize("name,T,H,I,E,k", [

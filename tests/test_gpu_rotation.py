@@ -16,7 +16,7 @@ import torch
 from gpu_cases import check_routing, dev_bf16, rel_l2, say, to_np
 from oracle import moe as omoe
 from oracle import rotation as orot
-from workloads import CONFIGS, gen
+from workloads import by_name, gen
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,7 @@ def test_rotated_outlier_layer_full_size(ops):
     from nvfp4_w4a4_mixture_amd import workload_io
     from nvfp4_w4a4_mixture_amd.layer import NVFP4MoELayer
 
-    cfg = CONFIGS[3]
+    cfg = by_name("outlier_128e")
     ws = cfg.weights
     say(f"rotated outlier layer: {cfg.describe()}")
     xb = gen.tokens(cfg)

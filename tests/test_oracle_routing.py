@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from oracle import routing
-from workloads import CONFIGS, gen
+from workloads import by_name, gen
 
 
 def _bf16(vals):
@@ -52,7 +52,7 @@ def test_logits_are_exact_bf16_products_in_float64():
 
 @pytest.fixture(scope="module")
 def tiny():
-    cfg = CONFIGS[0]
+    cfg = by_name("tiny")
     x = gen.tokens(cfg)
     wr = gen.router_weight(cfg.weights)
     b = gen.router_bias(cfg)

@@ -77,3 +77,11 @@ WEIGHT_SETS = {w.name: w for w in (TINY8, E80, E128_OUTLIER)}
 
 def config(i: int) -> LayerConfig:
     return CONFIGS[i]
+
+
+def by_name(name: str) -> LayerConfig:
+    """The workload with this name (tiny, decode, prefill_zipf, outlier_128e, long_reap)."""
+    for c in CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
