@@ -20,7 +20,7 @@ from gpu_cases import (bf16_round, check_routing, config_case, dev_bf16, gpu_lay
                        oracle_perm, random_case, rel_l2, say, to_np, untile_weight_scales)
 from oracle import nvfp4 as onv
 from oracle import routing as oroute
-from workloads import CONFIGS, by_name, gen
+from workloads import by_name, gen
 
 pytestmark = pytest.mark.gpu
 
