@@ -236,6 +236,14 @@ moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w,
                          const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
                          int64_t T, int64_t k, int64_t E, float* saliency, void* stream);
 
+/* moe_combine and reap_saliency in one launch (the same results): y from
+ * pair_out as moe_combine writes it, and saliency [E] as reap_saliency writes
+ * it.  Same arguments and requirements as the two calls. */
+moe_status moe_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype,
+                            void* y, const float* pair_sqnorm, const float* topk_w,
+                            const int32_t* expert_offsets, const int32_t* sorted_pair_ids, int64_t E,
+                            float* saliency, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* REAP one-shot pruning ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card,
  * introduction and "Pruning Setup": the routed experts of lowest REAP

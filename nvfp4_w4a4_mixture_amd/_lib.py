@@ -45,6 +45,7 @@ SIGNATURES = {
                                       _p, _p, _sz, _p]),
     "moe_combine": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p]),
     "reap_saliency": (_i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p]),
+    "moe_combine_reap": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i64, _p, _p]),
     "reap_prune_select": (_i32, [_p, _i64, _i64, _p, _p]),
     "moe_gather_experts": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
     "moe_shared_workspace_bytes": (_sz, [_i64, _i64, _i64]),

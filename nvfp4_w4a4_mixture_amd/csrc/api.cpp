@@ -368,6 +368,22 @@ moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w, const in
                   "reap_saliency");
 }
 
+moe_status moe_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y,
+                            const float* pair_sqnorm, const float* topk_w, const int32_t* expert_offsets,
+                            const int32_t* sorted_pair_ids, int64_t E, float* saliency, void* stream) {
+  const char* fn = "moe_combine_reap";
+  if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))
+    return fail(MOE_ERR_SHAPE, "%s: need T >= 0, k >= 1, H a positive multiple of 4, out_dtype 0 or 1", fn);
+  if (E < 1 || E > 256 || T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "%s: need 1 <= E <= 256", fn);
+  if (!expert_offsets || !saliency || (T > 0 && (!pair_out || !y || !pair_sqnorm || !topk_w || !sorted_pair_ids)))
+    return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (T > 0 && (!aligned(pair_out, 16) || !aligned(y, 16))) return fail(MOE_ERR_ALIGN, "%s: 16-byte alignment required", fn);
+  if (moe_status s = check_device()) return s;
+  return launched(moe::launch_combine_reap(pair_out, T, k, H, out_dtype, y, pair_sqnorm, topk_w, expert_offsets,
+                                           sorted_pair_ids, E, saliency, (hipStream_t)stream),
+                  fn);
+}
+
 moe_status reap_prune_select(const float* saliency, int64_t E, int64_t n_keep, int32_t* keep_ids, void* stream) {
   if (E < 1 || E > 256 || n_keep < 1 || n_keep > E)
     return fail(MOE_ERR_SHAPE, "reap_prune_select: need 1 <= n_keep <= E <= 256 (n_keep=%lld, E=%lld)",

@@ -15,12 +15,11 @@
 
 namespace moe {
 
+// y for one float4 column group i of the [T, H/4] output
 template <bool BF16_OUT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ pair_out,
-                                                      const float* __restrict__ add, int64_t T, int k, int64_t H,
-                                                      void* __restrict__ y) {
+__device__ __forceinline__ void combine_one(const float* __restrict__ pair_out, const float* __restrict__ add,
+                                            int64_t T, int k, int64_t H, void* __restrict__ y, int64_t i) {
   const int64_t h4 = H / 4;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * h4) return;
   const int64_t t = i / h4, c = i - t * h4;
   const float4* src = reinterpret_cast<const float4*>(pair_out) + (t * k) * h4 + c;
@@ -53,10 +52,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(256) void reap_kernel(const float* __restrict__ sq, const float* __restrict__ topk_w,
-                                                   const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ sorted, float* __restrict__ saliency) {
-  const int e = blockIdx.x;
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ pair_out,
+                                                      const float* __restrict__ add, int64_t T, int k, int64_t H,
+                                                      void* __restrict__ y) {
+  combine_one<BF16_OUT>(pair_out, add, T, k, H, y, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// saliency of expert e: its pairs walked in sorted order, FP64 sums in a fixed tree
+__device__ __forceinline__ void reap_one(const float* __restrict__ sq, const float* __restrict__ topk_w,
+                                         const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
+                                         float* __restrict__ saliency, int e) {
   const int b = offsets[e], n = offsets[e + 1] - b;
   double s = 0.0;
   for (int i = threadIdx.x; i < n; i += 256) {
@@ -71,6 +77,27 @@ __global__ __launch_bounds__(256) void reap_kernel(const float* __restrict__ sq,
     __syncthreads();
   }
   if (threadIdx.x == 0) saliency[e] = n > 0 ? (float)(red[0] / (double)n) : 0.0f;
+}
+
+__global__ __launch_bounds__(256) void reap_kernel(const float* __restrict__ sq, const float* __restrict__ topk_w,
+                                                   const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ sorted, float* __restrict__ saliency) {
+  reap_one(sq, topk_w, offsets, sorted, saliency, blockIdx.x);
+}
+
+// combine and REAP in one launch: blocks [0, nb) combine, blocks [nb, nb + E) one expert each
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_reap_kernel(const float* __restrict__ pair_out, int64_t T, int k,
+                                                           int64_t H, void* __restrict__ y, unsigned nb,
+                                                           const float* __restrict__ sq,
+                                                           const float* __restrict__ topk_w,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ sorted,
+                                                           float* __restrict__ saliency) {
+  if (blockIdx.x < nb)
+    combine_one<BF16_OUT>(pair_out, nullptr, T, k, H, y, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  else
+    reap_one(sq, topk_w, offsets, sorted, saliency, (int)(blockIdx.x - nb));
 }
 
 hipError_t launch_combine(const float* pair_out, const float* add, int64_t T, int64_t k, int64_t H, int out_dtype,
@@ -88,6 +115,20 @@ hipError_t launch_combine(const float* pair_out, const float* add, int64_t T, in
 hipError_t launch_reap(const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                        int64_t E, float* saliency, hipStream_t st) {
   hipLaunchKernelGGL(reap_kernel, dim3((unsigned)E), dim3(256), 0, st, sq, topk_w, offsets, sorted, saliency);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
+                               const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
+                               int64_t E, float* saliency, hipStream_t st) {
+  const unsigned nb = (unsigned)((T * (H / 4) + 255) / 256);
+  const dim3 grid(nb + (unsigned)E);
+  if (out_dtype == 0)
+    hipLaunchKernelGGL(combine_reap_kernel<true>, grid, dim3(256), 0, st, pair_out, T, (int)k, H, y, nb, sq, topk_w,
+                       offsets, sorted, saliency);
+  else
+    hipLaunchKernelGGL(combine_reap_kernel<false>, grid, dim3(256), 0, st, pair_out, T, (int)k, H, y, nb, sq, topk_w,
+                       offsets, sorted, saliency);
   return hipGetLastError();
 }
 

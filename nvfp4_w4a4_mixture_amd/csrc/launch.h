@@ -65,6 +65,9 @@ hipError_t launch_combine(const float* pair_out, const float* add, int64_t T, in
                           void* y, hipStream_t st);
 hipError_t launch_reap(const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                        int64_t E, float* saliency, hipStream_t st);
+hipError_t launch_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
+                               const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
+                               int64_t E, float* saliency, hipStream_t st);
 hipError_t launch_prune_select(const float* saliency, int64_t E, int64_t n_keep, int32_t* keep_ids, hipStream_t st);
 hipError_t launch_gather_blocks(const void* src, int64_t n_src, int64_t bytes, const int32_t* ids, int64_t n_ids,
                                 void* dst, hipStream_t st);

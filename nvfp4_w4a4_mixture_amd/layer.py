@@ -1,7 +1,7 @@
 """The routed NVFP4 W4A4 MoE layer as one object: the C-ABI calls in order.
 
 forward(x):  moe_route_quantize -> moe_nvfp4_gate_up_swiglu ->
-             moe_nvfp4_down_scatter -> moe_combine (-> reap_saliency)
+             moe_nvfp4_down_scatter -> moe_combine (moe_combine_reap with REAP)
 block output: moe_shared_expert on a second stream, joined by moe_combine_block
 (the two FFN calls are the stages of moe_nvfp4_grouped_ffn)
 All buffers for a given token count are allocated once and reused, so a
@@ -116,7 +116,7 @@ class NVFP4MoELayer:
         out.shared = self.shared  # the shared expert is kept whole
         return out
 
-    STAGES = ("route_quantize", "gate_up", "down", "combine", "reap")
+    STAGES = ("route_quantize", "gate_up", "down", "combine_reap")
 
     def forward(self, x_bf16: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16, reap: bool = False,
                 events: Optional[list] = None, block: bool = False) -> LayerOut:
@@ -158,17 +158,19 @@ class NVFP4MoELayer:
                                    r.sorted_pair_ids, r.topk_w, pair_out=b["pair_out"],
                                    pair_sqnorm=b["pair_sqnorm"] if reap else None, workspace=b["ffn_ws"])
         mark(3)
+        sal = None
         if block:
             torch.cuda.current_stream(self.device).wait_event(b["ev_shared"])
             ops.moe_combine_block(b["pair_out"], b["shared_out"], T, self.k, out_dtype, y=b["y"])
+            if reap:
+                sal = ops.reap_saliency(b["pair_sqnorm"], r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, self.k,
+                                        self.E, out=b["saliency"])
+        elif reap:  # the combine and the saliency in one launch
+            _, sal = ops.moe_combine_reap(b["pair_out"], T, self.k, b["pair_sqnorm"], r.topk_w, r.expert_offsets,
+                                          r.sorted_pair_ids, self.E, out_dtype, y=b["y"], saliency=b["saliency"])
         else:
             ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
         mark(4)
-        sal = None
-        if reap:
-            sal = ops.reap_saliency(b["pair_sqnorm"], r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, self.k,
-                                    self.E, out=b["saliency"])
-        mark(5)
         return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal,
                         b.get("shared_out"))
 

@@ -17,7 +17,7 @@ from ._lib import MoEError, check, lib  # noqa: F401
 
 __all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
            "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
-           "reap_prune_select", "moe_gather_experts", "moe_shared_workspace_bytes", "moe_shared_expert",
+           "moe_combine_reap", "reap_prune_select", "moe_gather_experts", "moe_shared_workspace_bytes", "moe_shared_expert",
            "moe_shared_gate_up", "moe_shared_down", "moe_combine_block", "hadamard_rotate_bf16",
            "moe_nvfp4_prepack_weights", "moe_nvfp4_unpack_weights",
            "moe_route_workspace_bytes", "moe_ffn_workspace_bytes", "moe_ffn_stage_workspace_bytes", "RouteOut"]
@@ -265,6 +265,22 @@ def moe_combine(pair_out: torch.Tensor, T: int, k: int, out_dtype: torch.dtype =
     st = lib().moe_combine(_p(pair_out), T, k, H, code, _p(y), _stream(stream))
     check(st, "moe_combine")
     return y
+
+
+def moe_combine_reap(pair_out: torch.Tensor, T: int, k: int, pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids,
+                     E: int, out_dtype: torch.dtype = torch.bfloat16, y=None, saliency=None, stream=None):
+    """moe_combine and reap_saliency in one launch: (y, saliency)."""
+    _need(pair_out, "pair_out", torch.float32)
+    H = pair_out.shape[1]
+    code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
+    if y is None:
+        y = torch.empty((T, H), dtype=out_dtype, device=pair_out.device)
+    if saliency is None:
+        saliency = torch.empty((E,), dtype=torch.float32, device=pair_out.device)
+    st = lib().moe_combine_reap(_p(pair_out), T, k, H, code, _p(y), _p(pair_sqnorm), _p(topk_w), _p(expert_offsets),
+                                _p(sorted_pair_ids), E, _p(saliency), _stream(stream))
+    check(st, "moe_combine_reap")
+    return y, saliency
 
 
 def reap_saliency(pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids, T: int, k: int, E: int, out=None,

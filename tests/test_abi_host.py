@@ -214,6 +214,14 @@ def test_shared_and_rotation_validation(L):
     assert r(P, 0, 256, 256, None, 16, P2, 256, None) == OK
 
 
+def test_combine_reap_validation(L):
+    f = L.moe_combine_reap
+    assert f(P, 4, 2, 66, 0, P, P, P, P, P, 8, P, None) == SHAPE
+    assert f(P, 4, 2, 64, 0, P, P, P, P, P, 0, P, None) == SHAPE
+    assert f(P, 4, 2, 64, 0, P, None, P, P, P, 8, P, None) == NULL
+    assert f(P, 4, 2, 64, 0, ctypes.c_void_p(0x10004), P, P, P, P, 8, P, None) == ALIGN
+
+
 def test_prepack_validation(L):
     for fn in (L.moe_nvfp4_prepack_weights, L.moe_nvfp4_unpack_weights):
         assert fn(P, P, 2, 24, 256, 1, P2, ctypes.c_void_p(0x30000), None) == SHAPE  # N % 16

@@ -376,3 +376,23 @@ def test_prepack_roundtrip_and_canonical_weights(ops):
     y1 = other(x, out_dtype=torch.float32).y
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("T", [12, 300])
+def test_combine_reap_equals_separate_calls(ops, T):
+    case = random_case(f"combine_reap_{T}", 41, T, 512, 256, 16, 4)
+    layer = gpu_layer(case)
+    say(f"combine + reap fused vs separate, T={T}")
+    out = layer(dev_bf16(case.x), out_dtype=torch.bfloat16, reap=True)  # the layer's fused launch
+    r = out.route
+    y2 = ops.moe_combine(out.pair_out, T, case.k, torch.bfloat16)
+    s2 = ops.reap_saliency(out.pair_sqnorm, r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, case.k, case.E)
+    torch.cuda.synchronize()
+    assert torch.equal(out.y, y2) and torch.equal(out.saliency, s2)
+    # no tokens: zero saliencies, nothing else written
+    e = torch.full((case.E,), 7.0, device="cuda")
+    off = torch.zeros((case.E + 1,), dtype=torch.int32, device="cuda")
+    empty = torch.empty((0, 512), dtype=torch.float32, device="cuda")
+    ops.moe_combine_reap(empty, 0, case.k, None, None, off, None, case.E, saliency=e)
+    torch.cuda.synchronize()
+    assert torch.all(e == 0)
