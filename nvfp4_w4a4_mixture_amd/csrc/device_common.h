@@ -98,18 +98,16 @@ __device__ __forceinline__ half8_t decode8(uint32_t codes, half2_t s2) {
   return r;
 }
 
-// {S, S} in FP16 for byte k of a dword of four E4M3 scale bytes, exactly and
-// without branches: an E4M3 byte b (sign 0) shifted left by 7 is the FP16 bit
-// pattern of S / 256 -- exponent field e lands in the FP16 exponent field, the
-// 3 mantissa bits on top of the FP16 mantissa, and the FP16 subnormal range
-// maps the E4M3 subnormals -- so one byte permute, one shift and one packed
-// multiply by 256 give the pair (FP16 subnormal inputs are not flushed).
+// {S, S} in FP16 for byte k of a dword of four E4M3 scale bytes.  The FP8
+// convert turns two E4M3 bytes into two FP16 values exactly (every E4M3 value,
+// subnormals included, is an FP16 value; byte 0 -> low half, checked for all
+// 127 finite codes on the device), and the broadcast of one half folds into the
+// op_sel of the multiply that consumes it, so the four scales of a dword cost
+// two converts.
 __device__ __forceinline__ half2_t scale_pair(uint32_t scales4, int k) {
-  const uint32_t sel = (uint32_t)k | (0x0Cu << 8) | ((uint32_t)k << 16) | (0x0Cu << 24);
-  const uint32_t t = __builtin_amdgcn_perm(scales4, scales4, sel) << 7;
-  const half2_t h = __builtin_bit_cast(half2_t, t);
-  const half2_t k256 = {(_Float16)256.0f, (_Float16)256.0f};
-  return h * k256;
+  const half2_t two = k >= 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales4, 1.0f, true)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales4, 1.0f, false);
+  return (k & 1) ? two.yy : two.xx;
 }
 
 // silu(g) = g / (1 + e^-g) from the hardware base-2 exponential and reciprocal
