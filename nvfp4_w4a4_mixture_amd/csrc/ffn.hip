@@ -928,18 +928,14 @@ hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool buil
   }
   const unsigned gy = (unsigned)ffn_max_tiles(T, a.k, E);
   static_assert(t8::BM == Tiled::BM && t8::BN == Tiled::BN && t8::kHcols == Tiled::kHcols, "tile shapes");
-  // the tiles need more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-  static const hipError_t attr_gu = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, Tiled::kLds);
-  static const hipError_t attr_dn = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, Tiled::kLds);
-  static const hipError_t attr8_dn = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_tiled8_kernel<kDown>),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize, t8::kLds);
-  if (attr_gu != hipSuccess) return attr_gu;
-  if (attr_dn != hipSuccess) return attr_dn;
-  if (attr8_dn != hipSuccess) return attr8_dn;
+  // the tiles need more than the default 64 KiB of dynamic LDS
+  if (hipError_t e = set_max_dynamic_lds(
+          reinterpret_cast<const void*>(&ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>), Tiled::kLds))
+    return e;
+  if (hipError_t e = set_max_dynamic_lds(
+          reinterpret_cast<const void*>(&ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>), Tiled::kLds))
+    return e;
+  if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ffn_tiled8_kernel<kDown>), t8::kLds)) return e;
   if (mode == kGateUp) {
     // four waves (measured on the 8192-token Zipf prefill: 3.08 ms against 3.20 ms with eight)
     const unsigned gx = (unsigned)(a.I / Tiled::kHcols);

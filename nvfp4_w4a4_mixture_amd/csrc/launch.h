@@ -6,7 +6,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace moe {
+
+// Raise a kernel's dynamic LDS limit above the default 64 KiB (gfx950 has 160 KiB
+// per CU), once per (kernel, device); later calls for the same pair return at once.
+inline hipError_t set_max_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  for (const auto& d : done)
+    if (d.first == kernel && d.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(kernel, dev);
+  return e;
+}
 
 // Arguments of one FFN stage (gate_up: A = x, B = w13; down: A = h, B = w2).
 struct FfnArgs {

@@ -120,10 +120,9 @@ __global__ __launch_bounds__(256) void hadamard_rotate_kernel(const uint16_t* __
 hipError_t launch_hadamard_rotate(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src, const float* signs,
                                   int64_t b, uint16_t* dst, int64_t ld_dst, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&hadamard_rotate_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     kRotMaxCols * (int)sizeof(double));
-  if (attr != hipSuccess) return attr;
+  if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&hadamard_rotate_kernel),
+                                         kRotMaxCols * (int)sizeof(double)))
+    return e;
   hipLaunchKernelGGL(hadamard_rotate_kernel, dim3((unsigned)rows), dim3(256), (size_t)cols * sizeof(double), st, src,
                      ld_src, (int)cols, signs, (int)b, __builtin_sqrt((double)b), dst, ld_dst);
   return hipGetLastError();

@@ -304,17 +304,13 @@ hipError_t launch_shared_stage(int mode, const uint16_t* a, int64_t lda, const u
   }
   const unsigned mtiles = (unsigned)((T + kDBM - 1) / kDBM);
   if (mode == kSharedGateUp) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&dense_tiled_kernel<kSharedGateUp>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        kDLds);
-    if (attr != hipSuccess) return attr;
+    if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&dense_tiled_kernel<kSharedGateUp>), kDLds))
+      return e;
     hipLaunchKernelGGL(dense_tiled_kernel<kSharedGateUp>, dim3((unsigned)(I / 128), mtiles), dim3(256), kDLds, st, a,
                        lda, w, T, K, I, h, I, (float*)nullptr, (int64_t)0);
   } else {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&dense_tiled_kernel<kSharedDown>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        kDLds);
-    if (attr != hipSuccess) return attr;
+    if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&dense_tiled_kernel<kSharedDown>), kDLds))
+      return e;
     hipLaunchKernelGGL(dense_tiled_kernel<kSharedDown>, dim3((unsigned)(H / kDBN), mtiles), dim3(256), kDLds, st, a,
                        lda, w, T, K, I, (uint16_t*)nullptr, (int64_t)0, out, H);
   }
