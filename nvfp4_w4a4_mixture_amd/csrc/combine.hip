@@ -4,7 +4,7 @@
 // renormalized sigmoid routing weights): y[t] = sum_j pair_out[t*k + j], in
 // j order, where pair_out already carries w_{t,j}; for the block output the
 // shared expert's FP32 row is added last.  HBM-bound: one float4 of y per
-// thread, k (+1) float4 reads.
+// thread, k (+1) float4 reads, issued eight at a time.
 //
 // REAP saliency (same card and section: mean(topk_weight * ||f_e(x)||_2) over
 // routed tokens, routing weights including routed_scaling_factor): one
@@ -23,13 +23,27 @@ __device__ __forceinline__ void combine_one(const float* __restrict__ pair_out, 
   if (i >= T * h4) return;
   const int64_t t = i / h4, c = i - t * h4;
   const float4* src = reinterpret_cast<const float4*>(pair_out) + (t * k) * h4 + c;
-  float4 s = src[0];
-  for (int j = 1; j < k; ++j) {
-    const float4 v = src[(int64_t)j * h4];
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
+  // the k rows in chunks of 8 loads issued together, summed in j order
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    const int n = k - j0 < 8 ? k - j0 : 8;
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < n) v[u] = src[(int64_t)(j0 + u) * h4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < n) {
+        if (j0 + u == 0) {
+          s = v[u];
+        } else {
+          s.x += v[u].x;
+          s.y += v[u].y;
+          s.z += v[u].z;
+          s.w += v[u].w;
+        }
+      }
+    }
   }
   if (add != nullptr) {  // the block output: routed combine, then the shared expert
     const float4 v = reinterpret_cast<const float4*>(add)[i];
