@@ -33,6 +33,11 @@ namespace moe {
 
 constexpr int kRotMaxCols = 16384;
 
+// LDS slot of row element i: one FP64 of padding per 32 elements, so that the
+// 8-element groups of neighbouring threads do not fall on the same banks
+__device__ __forceinline__ int lds_slot(int i) { return i + (i >> 5); }
+constexpr int lds_doubles(int cols) { return cols + cols / 32; }
+
 __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
   float f = (float)d;  // round to nearest even
   uint32_t u = __float_as_uint(f);
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(256) void hadamard_rotate_kernel(const uint16_t* __
     }
     butterflies8(v, 1, first);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) row[c + j] = v[j];
+    for (int j = 0; j < 8; ++j) row[lds_slot(c + j)] = v[j];
   }
   // later passes: element j of group m sits at base(m) + j * stride, base(m) = m with 3 zero
   // bits inserted at bit log2(stride)
@@ -99,10 +104,10 @@ __global__ __launch_bounds__(256) void hadamard_rotate_kernel(const uint16_t* __
       const int base = ((m - lo) << 3) | lo;
       double v[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = row[base + j * stride];
+      for (int j = 0; j < 8; ++j) v[j] = row[lds_slot(base + j * stride)];
       butterflies8(v, stride, b);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) row[base + j * stride] = v[j];
+      for (int j = 0; j < 8; ++j) row[lds_slot(base + j * stride)] = v[j];
     }
   }
   __syncthreads();
@@ -112,7 +117,8 @@ __global__ __launch_bounds__(256) void hadamard_rotate_kernel(const uint16_t* __
     u32x4_t o;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      o[j] = f64_to_bf16_rne(row[c + 2 * j] / sqrtb) | (f64_to_bf16_rne(row[c + 2 * j + 1] / sqrtb) << 16);
+      o[j] = f64_to_bf16_rne(row[lds_slot(c + 2 * j)] / sqrtb) |
+             (f64_to_bf16_rne(row[lds_slot(c + 2 * j + 1)] / sqrtb) << 16);
     *reinterpret_cast<u32x4_t*>(d + c) = o;
   }
 }
@@ -121,9 +127,10 @@ hipError_t launch_hadamard_rotate(const uint16_t* src, int64_t rows, int64_t col
                                   int64_t b, uint16_t* dst, int64_t ld_dst, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&hadamard_rotate_kernel),
-                                         kRotMaxCols * (int)sizeof(double)))
+                                         lds_doubles(kRotMaxCols) * (int)sizeof(double)))
     return e;
-  hipLaunchKernelGGL(hadamard_rotate_kernel, dim3((unsigned)rows), dim3(256), (size_t)cols * sizeof(double), st, src,
+  const size_t lds = (size_t)lds_doubles((int)cols) * sizeof(double);
+  hipLaunchKernelGGL(hadamard_rotate_kernel, dim3((unsigned)rows), dim3(256), lds, st, src,
                      ld_src, (int)cols, signs, (int)b, __builtin_sqrt((double)b), dst, ld_dst);
   return hipGetLastError();
 }
