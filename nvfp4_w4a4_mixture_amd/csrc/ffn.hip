@@ -255,23 +255,6 @@ struct TiledShape {
   static constexpr int kLoadsPerStage = kACodeOps + kAScaleOps + kBCodeOps + kBScaleOps;
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <int MODE, int WM, int WN, int NS>
 __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
   using S = TiledShape<WM, WN, NS>;

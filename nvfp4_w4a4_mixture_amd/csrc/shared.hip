@@ -15,13 +15,10 @@
 //    MFMA with the tokens as M; the four waves meet in LDS and the workgroup
 //    writes one FP32 partial per K split.  A finalize pass sums the splits in
 //    order (and applies SwiGLU + BF16 rounding for stage 1).
-//  * dense_tiled_kernel (T > 16): MFMA-bound.  256 x 256 tile per workgroup,
-//    2 x 2 waves of 128 x 128 (16 32x32x16 accumulators each), 64-k stages in
-//    an LDS double buffer filled from registers (the next stage's global loads
-//    are in flight while the current one is multiplied), 16-byte chunks
-//    swizzled by row so that fragment reads and stores are bank-conflict
-//    free.  Stage 1's tile pairs 64 gate rows with the 64 up rows of the same
-//    h columns in each wave, so SwiGLU is applied in registers.
+//  * dense_ring_kernel (T > 16): 256 x 256 tile per workgroup, 2 x 4 waves of
+//    128 x 64, operand tiles streamed into a 4-stage LDS ring by DMA.  Stage
+//    1's tile pairs 32 gate rows with the 32 up rows of the same h columns in
+//    each wave, so SwiGLU is applied in registers.
 #include "device_common.h"
 #include "launch.h"
 
@@ -130,117 +127,142 @@ __global__ __launch_bounds__(256) void dense_sum_finalize_kernel(const float* __
 }
 
 // ---------------------------------------------------------------------------
-// tiled kernel
+// tiled kernel with a DMA ring (the production path for T > 16)
+//
+// 256 x 256 workgroup tile, eight waves in 2 (M) x 4 (N), each owning 128 x 64
+// (4 x 2 accumulators of 32 x 32), two waves per SIMD so that one wave's LDS
+// reads overlap the other's MFMAs.  Operand tiles go from HBM straight into a
+// 4-stage LDS ring (global_load_lds, 32 k per stage: 64 B per row in four
+// 16-byte slots, chunk c of row r in slot c ^ ((r >> 2) & 3)); each wave reads
+// its fragments of a stage in one asm block that waits only for LDS, so the
+// DMA of later stages stays in flight.
 
-constexpr int kDBM = 256, kDBN = 256, kDBK = 64;
-constexpr int kDTileBytes = kDBM * kDBK * 2;        // one operand's stage: 256 rows x 128 B
-constexpr int kDStage = 2 * kDTileBytes;            // A then B
-constexpr int kDLds = 2 * kDStage;                  // double buffer, 128 KB
-
-// 16-byte chunk c of row r is stored in slot c ^ ((r >> 1) & 7): the 16 rows a
-// fragment read touches at one chunk, and the 2 rows of 8 chunks a store
-// group writes, land in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int dslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+namespace dr {
+constexpr int BM = 256, BN = 256, NS = 4;
+constexpr int kTile = BM * 64;           // one operand's stage: 256 rows x 32 k x 2 B
+constexpr int kStage = 2 * kTile;        // A then B
+constexpr int kLds = NS * kStage;        // 128 KiB
+constexpr int kLoadsPerStage = 2 + 2;    // 16-byte DMA per wave and stage: A, B
+}  // namespace dr
 
 template <int MODE>
-__global__ __launch_bounds__(256) void dense_tiled_kernel(const uint16_t* __restrict__ a, int64_t lda,
-                                                          const uint16_t* __restrict__ w, int64_t T, int64_t K,
-                                                          int64_t I, uint16_t* __restrict__ h, int64_t ldh,
-                                                          float* __restrict__ out, int64_t ldo) {
+__global__ __launch_bounds__(512) void dense_ring_kernel(const uint16_t* __restrict__ a, int64_t lda,
+                                                         const uint16_t* __restrict__ w, int64_t T, int64_t K,
+                                                         int64_t I, uint16_t* __restrict__ h, int64_t ldh,
+                                                         float* __restrict__ out, int64_t ldo) {
+  using namespace dr;
   const int nt = blockIdx.x, mt = blockIdx.y;
-  const int64_t m0 = (int64_t)mt * kDBM;
+  const int64_t m0 = (int64_t)mt * BM;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   const int r = lane & 31, g = lane >> 5;
 
-  // B tile row n -> weight row.  Stage 1: wave wn's 128 rows are h columns
-  // nt*128 + wn*64 + 0..63 as gate rows (n % 128 < 64) then as up rows.
+  // B tile row n -> weight row.  Stage 1: N wave n / 64 owns h columns nt*128 + 32*(n/64) + 0..31,
+  // as gate rows (n % 64 < 32) and as up rows.
   auto b_row = [&](int n) -> int64_t {
     if (MODE == kSharedGateUp) {
-      const int wv = n >> 7, j = (n & 127) >> 5, cc = n & 31;
-      return (j < 2 ? 0 : I) + (int64_t)nt * 128 + wv * 64 + 32 * (j & 1) + cc;
+      const int wv = n >> 6, j = (n >> 5) & 1, cc = n & 31;
+      return (j ? I : 0) + (int64_t)nt * 128 + 32 * wv + cc;
     }
-    return (int64_t)nt * kDBN + n;
+    return (int64_t)nt * BN + n;
   };
-  // global -> register loads: load i of a thread covers row 32 i + tid / 8, chunk tid % 8
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const uint16_t* ag[8];
-  const uint16_t* bg[8];
-  uint32_t lds_off[8];
+  // 16-byte DMA i (0, 1) of this wave: rows 16 q .. 16 q + 15, q = 8 i + wave; lane -> row 16 q + lane / 4,
+  // LDS slot lane % 4 holding chunk slot ^ ((row >> 2) & 3)
+  uint32_t a_off[2], b_off[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * i + lrow;
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (8 * i + wave) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     const int64_t t = m0 + row < T ? m0 + row : T - 1;  // rows past T repeat the last token; never stored
-    ag[i] = a + t * lda + 8 * lchunk;
-    bg[i] = w + b_row(row) * K + 8 * lchunk;
-    lds_off[i] = (uint32_t)(row * 128 + 16 * dslot(row, lchunk));
+    a_off[i] = (uint32_t)(t * lda * 2) + 16 * chunk;
+    b_off[i] = (uint32_t)(b_row(row) * K * 2) + 16 * chunk;
   }
-  u32x4_t ra[8], rb[8];
-  auto gload = [&](int64_t st) {
+  auto issue = [&](int64_t st) {
+    unsigned char* base = smem + (int)(st % NS) * kStage;
+    const unsigned char* ag = reinterpret_cast<const unsigned char*>(a) + st * 64;
+    const unsigned char* bg = reinterpret_cast<const unsigned char*>(w) + st * 64;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(ag[i] + st * kDBK);
+    for (int i = 0; i < 2; ++i) dma16(ag + a_off[i], base + (8 * i + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(bg[i] + st * kDBK);
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* base = smem + buf * kDStage;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(base + lds_off[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(base + kDTileBytes + lds_off[i]) = rb[i];
+    for (int i = 0; i < 2; ++i) dma16(bg + b_off[i], base + kTile + (8 * i + wave) * 1024);
   };
 
-  float16_t acc[4][4];
+  float16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // fragment i of this wave: rows wm*128 + 32 i + r (A), wn*128 + 32 j + r (B);
-  // k-step s of a stage: chunk 2 s + g.  (32 i + r) >> 1 & 7 == (r >> 1) & 7.
-  const int arow = wm * 128 + r, brow = wn * 128 + r;
-  auto frag = [&](const unsigned char* base, int row, int s) -> bf16x8_t {
-    return as_bf16x8(*reinterpret_cast<const u32x4_t*>(base + row * 128 + 16 * dslot(r, 2 * s + g)));
-  };
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const uint32_t a_lane = (uint32_t)(wm * 128 + r) * 64u;
+  const uint32_t b_lane = (uint32_t)kTile + (uint32_t)(wn * 64 + r) * 64u;
+  // k-step s (0, 1) of a stage: chunk 2 s + g; rows 32 apart share (r >> 2) & 3
+  const uint32_t slot0 = 16u * (uint32_t)((2 * 0 + g) ^ ((r >> 2) & 3));
+  const uint32_t slot1 = 16u * (uint32_t)((2 * 1 + g) ^ ((r >> 2) & 3));
 
-  const int64_t nst = K / kDBK;
-  gload(0);
-  lstore(0);
-  if (nst > 1) gload(1);
+  const int64_t nst = K / 32;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nst) issue(p);
   for (int64_t st = 0; st < nst; ++st) {
-    __syncthreads();  // stage st is in buffer st & 1 for every wave; buffer (st + 1) & 1 is free
-    const unsigned char* base = smem + (int)(st & 1) * kDStage;
-    bf16x8_t fa[2][4], fb[2][4];
+    const int64_t ahead = nst - 1 - st;
+    if (ahead >= NS - 2) wait_vmcnt<kLoadsPerStage * (NS - 2)>();
+    else if (ahead == 1) wait_vmcnt<kLoadsPerStage>();
+    else wait_vmcnt<0>();
+    // bare s_barrier: every wave's DMA for stage st has landed and stage st-1's buffer is read
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const uint32_t sb = lds_base + (uint32_t)(st % NS) * kStage;
+    const uint32_t a0 = sb + a_lane + slot0, a1 = sb + a_lane + slot1;
+    const uint32_t b0 = sb + b_lane + slot0, b1 = sb + b_lane + slot1;
+    u32x4_t fa[2][4], fb[2][2];
+    asm volatile(
+        "ds_read_b128 %0, %12 offset:0\n"
+        "ds_read_b128 %1, %12 offset:2048\n"
+        "ds_read_b128 %2, %12 offset:4096\n"
+        "ds_read_b128 %3, %12 offset:6144\n"
+        "ds_read_b128 %4, %13 offset:0\n"
+        "ds_read_b128 %5, %13 offset:2048\n"
+        "ds_read_b128 %6, %14 offset:0\n"
+        "ds_read_b128 %7, %14 offset:2048\n"
+        "ds_read_b128 %8, %14 offset:4096\n"
+        "ds_read_b128 %9, %14 offset:6144\n"
+        "ds_read_b128 %10, %15 offset:0\n"
+        "ds_read_b128 %11, %15 offset:2048\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[0][2]), "=&v"(fa[0][3]), "=&v"(fb[0][0]), "=&v"(fb[0][1]),
+          "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fa[1][2]), "=&v"(fa[1][3]), "=&v"(fb[1][0]), "=&v"(fb[1][1])
+        : "v"(a0), "v"(b0), "v"(a1), "v"(b1)
+        : "memory");
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = frag(base, arow + 32 * i, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = frag(base + kDTileBytes, brow + 32 * j, 0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[cur ^ 1][i] = frag(base, arow + 32 * i, s + 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[cur ^ 1][j] = frag(base + kDTileBytes, brow + 32 * j, s + 1);
-      }
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-    }
-    if (st + 1 < nst) {
-      lstore((int)((st + 1) & 1));
-      if (st + 2 < nst) gload(st + 2);
-    }
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[s2][i]), as_bf16x8(fb[s2][j]), acc[i][j],
+                                                              0, 0, 0);
   }
 
-  // ---- epilogues.  acc[i][j][e]: row wm*128 + 32 i + 8 (e/4) + 4 g + e%4, column r of tile j
+  // ---- epilogues.  acc[i][j][e]: row wm*128 + 32 i + 8 (e/4) + 4 g + e%4, column r of B fragment j
   if (MODE == kSharedGateUp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t t = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (t < T) {
+          const int64_t c = (int64_t)nt * 128 + wn * 32 + r;
+          h[t * ldh + c] = (uint16_t)f32_to_bf16_rne(silu(acc[i][0][e]) * acc[i][1][e]);
+        }
+      }
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -248,26 +270,14 @@ __global__ __launch_bounds__(256) void dense_tiled_kernel(const uint16_t* __rest
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t t = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (t < T) {
-            const int64_t c = (int64_t)nt * 128 + wn * 64 + 32 * j + r;
-            h[t * ldh + c] = (uint16_t)f32_to_bf16_rne(silu(acc[i][j][e]) * acc[i][j + 2][e]);
-          }
-        }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int64_t t = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (t < T) out[t * ldo + (int64_t)nt * kDBN + wn * 128 + 32 * j + r] = acc[i][j][e];
+          if (t < T) out[t * ldo + (int64_t)nt * BN + wn * 64 + 32 * j + r] = acc[i][j][e];
         }
   }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
+
 
 static int small_splits(int64_t K) { return (int)((K + kSmallKSplit - 1) / kSmallKSplit); }
 
@@ -302,16 +312,16 @@ hipError_t launch_shared_stage(int mode, const uint16_t* a, int64_t lda, const u
     }
     return hipGetLastError();
   }
-  const unsigned mtiles = (unsigned)((T + kDBM - 1) / kDBM);
+  const unsigned mtiles = (unsigned)((T + dr::BM - 1) / dr::BM);
   if (mode == kSharedGateUp) {
-    if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&dense_tiled_kernel<kSharedGateUp>), kDLds))
+    if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&dense_ring_kernel<kSharedGateUp>), dr::kLds))
       return e;
-    hipLaunchKernelGGL(dense_tiled_kernel<kSharedGateUp>, dim3((unsigned)(I / 128), mtiles), dim3(256), kDLds, st, a,
+    hipLaunchKernelGGL(dense_ring_kernel<kSharedGateUp>, dim3((unsigned)(I / 128), mtiles), dim3(512), dr::kLds, st, a,
                        lda, w, T, K, I, h, I, (float*)nullptr, (int64_t)0);
   } else {
-    if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&dense_tiled_kernel<kSharedDown>), kDLds))
+    if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&dense_ring_kernel<kSharedDown>), dr::kLds))
       return e;
-    hipLaunchKernelGGL(dense_tiled_kernel<kSharedDown>, dim3((unsigned)(H / kDBN), mtiles), dim3(256), kDLds, st, a,
+    hipLaunchKernelGGL(dense_ring_kernel<kSharedDown>, dim3((unsigned)(H / dr::BN), mtiles), dim3(512), dr::kLds, st, a,
                        lda, w, T, K, I, (uint16_t*)nullptr, (int64_t)0, out, H);
   }
   return hipGetLastError();
