@@ -138,6 +138,32 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 4, 0, 0);
 }
 
+// The same DMAs written as inline asm, in the SGPR-base form (wave-uniform
+// 64-bit base, 32-bit lane offset).  The compiler then does not count them as
+// outstanding LDS writes, so the LDS reads it issues itself get no blanket
+// vmcnt(0); the caller orders every read of a DMA'd buffer with its own vmcnt
+// wait and a barrier.  The instruction has no destination register (it
+// writes LDS at M0 + 16 * lane, or 4 * lane), and M0 is declared as an output
+// so the compiler knows the asm redefines it.  lds and sbase must be
+// wave-uniform.
+__device__ __forceinline__ void dma16_async(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t m0;
+  asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2"
+               : "={m0}"(m0)
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4_async(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t m0;
+  asm volatile("s_mov_b32 m0, %3\n\tglobal_load_lds_dword %1, %2"
+               : "={m0}"(m0)
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+
+// Every LDS access this wave has issued has completed; then the workgroup barrier.
+__device__ __forceinline__ void barrier_after_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

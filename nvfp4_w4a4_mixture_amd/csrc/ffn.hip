@@ -26,10 +26,13 @@
 //    16x16x32 MFMA; the waves' partial sums meet in LDS.
 //  * ffn_tiled_kernel (any M): one workgroup per (m-tile of an expert's
 //    pairs, n-tile of weight rows); A and B FP4 tiles go from HBM straight
-//    into a ring of LDS stages (global_load_lds, no register staging) that
-//    keeps several stages in flight; 32x32x16 MFMA, 2x2 waves of 128x128
-//    each (16 accumulator tiles per wave: 8 decoded fragments feed 16 MFMAs
-//    per k-step).
+//    into a 4-stage ring of LDS stages (global_load_lds, no register staging);
+//    32x32x16 MFMA, 2x2 waves of 128x128 each (16 accumulator tiles per wave:
+//    8 decoded fragments feed 16 MFMAs per k-step).  One barrier per stage,
+//    mid-stage; the fragment reads of the next half-stage and the FP4 decode
+//    of the next k-step run beside the current k-step's MFMAs.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -358,110 +361,190 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
   const uint32_t slot_q0 = (uint32_t)((2 * g) ^ ((r >> 2) & 3)), slot_q1 = (uint32_t)((2 * g + 1) ^ ((r >> 2) & 3));
   (void)lds_base; (void)a_lane; (void)b_lane; (void)as_lane; (void)bs_lane; (void)slot_q0; (void)slot_q1;
 
-  // NS-stage ring: stages st+1 .. st+NS-2 stay in flight while stage st is
-  // consumed; one barrier per stage both publishes stage st and frees the
-  // buffer of stage st-1 for the next DMA.
   const int64_t nst = K / 128;
+  if constexpr (WM == 4 && WN == 4) {
+    // Pipelined ring.  The DMA is issued as inline asm, so the compiler issues
+    // the fragment reads itself, with per-read lgkmcnt waits, and never drains
+    // the DMA still in flight.  Each 128-k stage is two halves of four 16-k
+    // sub-steps: the second half's code words are read during the first half,
+    // and after the one barrier per stage (mid-stage) the next stage's
+    // first-half words and scales are read during the second half.  The decode
+    // of sub-step n + 1 runs beside the 16 MFMAs of sub-step n throughout,
+    // across stage boundaries too.
+    //
+    // Ring: the prologue fills all NS slots.  At the mid-stage barrier of stage
+    // st every wave has finished its reads of slot st % NS (lgkmcnt(0) before
+    // the barrier) and waited for its DMA of stage st + 1, so stage st + NS is
+    // issued into slot st % NS right after it.
+    constexpr int L = S::kLoadsPerStage;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
+    auto issue_async = [&](int64_t st) {
+      const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(st % NS) * (uint32_t)S::kStage);
+      const uint8_t* ac = a.a_codes + st * 64;  // 128 k per stage
+      const uint8_t* as = a.a_scales + st * 8;
+      const uint8_t* bc = b_code_expert + st * 64;
+      const uint8_t* bs = b_scale_expert + st * 128;
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nst) issue(p);
-  for (int64_t st = 0; st < nst; ++st) {
-    const int64_t ahead = nst - 1 - st;  // stages issued after st that may still be in flight
-    if (ahead >= NS - 2) wait_vmcnt<S::kLoadsPerStage * (NS - 2)>();
-    else if (NS >= 4 && ahead == 2) wait_vmcnt<S::kLoadsPerStage * 2>();
-    else if (NS >= 3 && ahead == 1) wait_vmcnt<S::kLoadsPerStage>();
+      for (int i = 0; i < S::kACodeOps; ++i) dma16_async(ac, a_code_off[i], sb + (4 * i + wave_u) * 1024u);
+#pragma unroll
+      for (int i = 0; i < S::kAScaleOps; ++i)
+        dma4_async(as, a_scale_off[i], sb + (uint32_t)S::kACodeBytes + (4 * i + wave_u) * 256u);
+#pragma unroll
+      for (int i = 0; i < S::kBCodeOps; ++i)
+        dma16_async(bc, b_code_off[i], sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (4 * i + wave_u) * 1024u);
+#pragma unroll
+      for (int i = 0; i < S::kBScaleOps; ++i)
+        dma4_async(bs, b_scale_off[i],
+                   sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (4 * i + wave_u) * 256u);
+    };
+    // this lane's fragment words of one half (fragment i of a row block sits
+    // 2048 B = 32 rows after fragment i-1) and its scale words (256 B apart)
+    auto load_half = [&](int64_t st, uint32_t slot, u32x4_t* fa, u32x4_t* fb) {
+      const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const u32x4_t*>(smem + sb + a_lane + 16u * slot + 2048u * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const u32x4_t*>(smem + sb + b_lane + 16u * slot + 2048u * j);
+    };
+    auto load_scales = [&](int64_t st, uint32_t* sa, uint32_t* sbv) {
+      const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(smem + sb + as_lane + 256u * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sbv[j] = *reinterpret_cast<const uint32_t*>(smem + sb + bs_lane + 256u * j);
+    };
+    // sub-step ss (q = ss / 4 half, dword ss % 4) uses scale byte 2 q + (ss % 4) / 2 of the lane's word
+    half8_t da[2][4], db[2][4];
+    auto decode = [&](int buf, const u32x4_t* fa, const u32x4_t* fb, int w, const uint32_t* sa, const uint32_t* sbv,
+                      int sbyte) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][w], scale_pair(sa[i], sbyte));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) db[buf][j] = decode8(fb[j][w], scale_pair(sbv[j], sbyte));
+    };
+    // the 16 MFMAs of a sub-step, each followed by a slice of the next
+    // sub-step's decode and, for the first n_ds, by one of the LDS reads just
+    // issued in program order (so they go out early instead of just before use)
+    auto mfma16 = [&](int buf, int n_ds) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[buf][i], db[buf][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (m < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+    };
+
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+      if (p < nst) issue_async(p);
+    // stage 0 has landed; up to NS - 1 later stages may stay in flight
+    if (nst >= 4) wait_vmcnt<3 * L>();
+    else if (nst == 3) wait_vmcnt<2 * L>();
+    else if (nst == 2) wait_vmcnt<L>();
     else wait_vmcnt<0>();
-    // Bare s_barrier: this wave's DMA for stage st has landed (vmcnt above), and
-    // its reads of stage st-1's buffer were consumed in the previous iteration.
-    // __syncthreads() would also wait for every DMA still in flight.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const unsigned char* base = smem + (int)(st % NS) * S::kStage;
-    if constexpr (WM == 4 && WN == 4) {
-      // The stage's LDS reads in two asm blocks (k 0..63, then k 64..127), each
-      // ending in its own lgkmcnt(0).  Issued by the compiler, an LDS read after
-      // the in-flight ring DMA would get a conservative vmcnt(0) (it cannot tell
-      // the ring stages apart), draining the DMA of the later stages too.
-      // Fragment i of a row block sits 2048 B (32 rows) after fragment i-1; its
-      // scale word 256 B after.
-      const uint32_t sb = lds_base + (uint32_t)(st % NS) * S::kStage;
-      const uint32_t a0 = sb + a_lane + 16u * slot_q0, a1 = sb + a_lane + 16u * slot_q1;
-      const uint32_t b0 = sb + b_lane + 16u * slot_q0, b1 = sb + b_lane + 16u * slot_q1;
-      const uint32_t as_addr = sb + as_lane, bs_addr = sb + bs_lane;
-      u32x4_t fa[4], fb[4];
-      uint32_t sa[4], sbv[4];
-      asm volatile(
-          "ds_read_b32 %8, %18 offset:0\n"
-          "ds_read_b32 %9, %18 offset:256\n"
-          "ds_read_b32 %10, %18 offset:512\n"
-          "ds_read_b32 %11, %18 offset:768\n"
-          "ds_read_b32 %12, %19 offset:0\n"
-          "ds_read_b32 %13, %19 offset:256\n"
-          "ds_read_b32 %14, %19 offset:512\n"
-          "ds_read_b32 %15, %19 offset:768\n"
-          "ds_read_b128 %0, %16 offset:0\n"
-          "ds_read_b128 %1, %16 offset:2048\n"
-          "ds_read_b128 %2, %16 offset:4096\n"
-          "ds_read_b128 %3, %16 offset:6144\n"
-          "ds_read_b128 %4, %17 offset:0\n"
-          "ds_read_b128 %5, %17 offset:2048\n"
-          "ds_read_b128 %6, %17 offset:4096\n"
-          "ds_read_b128 %7, %17 offset:6144\n"
-          "s_waitcnt lgkmcnt(0)\n"
-          : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
-            "=&v"(fb[3]), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sbv[0]), "=&v"(sbv[1]),
-            "=&v"(sbv[2]), "=&v"(sbv[3])
-          : "v"(a0), "v"(b0), "v"(as_addr), "v"(bs_addr)
-          : "memory");
-      // Sub-steps ss = 0..7 (q = ss / 4 half, s = ss % 4 dword): the operands of
-      // sub-step ss + 1 are decoded while the 16 MFMAs of sub-step ss run.
-      half8_t da[2][4], db[2][4];
-      auto decode_step = [&](int ss, int buf) {
-        const int sbyte = 2 * (ss >> 2) + ((ss & 3) >> 1);
+    barrier_after_lds();
+    u32x4_t c0a[4], c0b[4];
+    uint32_t sa[4], sbv[4];
+    load_half(0, slot_q0, c0a, c0b);
+    load_scales(0, sa, sbv);
+    decode(0, c0a, c0b, 0, sa, sbv, 0);
+    // One stage; MORE: a stage follows, ISSUE: stage st + NS exists.  The
+    // loop is peeled on both so the steady-state body has no branch, and the
+    // compiler's LDS wait counts stay exact.
+    auto stage = [&](int64_t st, auto more_c, auto issue_c) {
+      constexpr bool kMore = decltype(more_c)::value, kIssue = decltype(issue_c)::value;
+      // Each sub-step is its own scheduling region (sched_barrier), so no
+      // decode, and no scale convert in particular, is hoisted next to the
+      // LDS read it depends on; the reads are issued at the top of a half.
+      u32x4_t c1a[4], c1b[4];
+      __builtin_amdgcn_sched_barrier(0);
+      load_half(st, slot_q1, c1a, c1b);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][ss & 3], scale_pair(sa[i], sbyte));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) db[buf][j] = decode8(fb[j][ss & 3], scale_pair(sbv[j], sbyte));
-      };
-      auto mfma_step = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[buf][i], db[buf][j], acc[i][j], 0, 0, 0);
-      };
-      decode_step(0, 0);
-#pragma unroll
-      for (int ss = 0; ss < 8; ++ss) {
-        const int cur = ss & 1;
-        if (ss == 3) {
-          asm volatile(
-              "ds_read_b128 %0, %8 offset:0\n"
-              "ds_read_b128 %1, %8 offset:2048\n"
-              "ds_read_b128 %2, %8 offset:4096\n"
-              "ds_read_b128 %3, %8 offset:6144\n"
-              "ds_read_b128 %4, %9 offset:0\n"
-              "ds_read_b128 %5, %9 offset:2048\n"
-              "ds_read_b128 %6, %9 offset:4096\n"
-              "ds_read_b128 %7, %9 offset:6144\n"
-              "s_waitcnt lgkmcnt(0)\n"
-              : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(fb[2]),
-                "=&v"(fb[3])
-              : "v"(a1), "v"(b1)
-              : "memory");
+      for (int ss = 0; ss < 4; ++ss) {
+        if (ss > 0) __builtin_amdgcn_sched_barrier(0);
+        if (ss < 3) decode((ss + 1) & 1, c0a, c0b, ss + 1, sa, sbv, (ss + 1) >> 1);
+        else decode(0, c1a, c1b, 0, sa, sbv, 2);
+        mfma16(ss & 1, ss == 0 ? 8 : 0);
+      }
+      u32x4_t n0a[4], n0b[4];
+      uint32_t nsa[4], nsb[4];
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kMore) {
+        // stage st + 1 has landed; the stages issued after it may stay in flight
+        if constexpr (kIssue) {
+          wait_vmcnt<2 * L>();
+        } else {
+          const int64_t ahead = nst - 2 - st;
+          if (ahead >= 2) wait_vmcnt<2 * L>();
+          else if (ahead == 1) wait_vmcnt<L>();
+          else wait_vmcnt<0>();
         }
-        if (ss + 1 < 8) decode_step(ss + 1, cur ^ 1);
-        mfma_step(cur);
-        // schedule: each of the 16 MFMAs followed by a slice of the next decode
+        barrier_after_lds();
+        if constexpr (kIssue) issue_async(st + NS);
+        load_half(st + 1, slot_q0, n0a, n0b);
+        load_scales(st + 1, nsa, nsb);
+      }
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      for (int ss = 4; ss < 8; ++ss) {
+        if (ss > 4) __builtin_amdgcn_sched_barrier(0);
+        if (ss < 7) {
+          decode((ss + 1) & 1, c1a, c1b, (ss + 1) & 3, sa, sbv, 2 + (((ss + 1) & 3) >> 1));
+        } else if (kMore) {
+          // Pin the next stage's words here: instruction selection would
+          // otherwise place their (pure) converts right after the reads, and
+          // the wave would wait for the LDS there.
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            asm volatile("" : "+v"(nsa[i]), "+v"(nsb[i]));
+            asm volatile("" : "+v"(n0a[i]), "+v"(n0b[i]));
+          }
+          decode(0, n0a, n0b, 0, nsa, nsb, 0);
+        }
+        mfma16(ss & 1, (kMore && ss == 4) ? 12 : 0);
+      }
+      if constexpr (kMore) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c0a[i] = n0a[i];
+          c0b[i] = n0b[i];
+          sa[i] = nsa[i];
+          sbv[i] = nsb[i];
         }
       }
-    } else {
+    };
+    int64_t st = 0;
+    for (; st + NS < nst; ++st) stage(st, std::true_type{}, std::true_type{});
+    for (; st + 1 < nst; ++st) stage(st, std::true_type{}, std::false_type{});
+    stage(st, std::false_type{}, std::false_type{});
+    wait_vmcnt<0>();  // nothing is in flight here; the epilogue's barrier does not know of the asm DMA
+  } else {
+    // NS-stage ring: stages st+1 .. st+NS-2 stay in flight while stage st is
+    // consumed; one barrier per stage both publishes stage st and frees the
+    // buffer of stage st-1 for the next DMA.
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nst) issue(p);
+    for (int64_t st = 0; st < nst; ++st) {
+      const int64_t ahead = nst - 1 - st;  // stages issued after st that may still be in flight
+      if (ahead >= NS - 2) wait_vmcnt<S::kLoadsPerStage * (NS - 2)>();
+      else if (NS >= 4 && ahead == 2) wait_vmcnt<S::kLoadsPerStage * 2>();
+      else if (NS >= 3 && ahead == 1) wait_vmcnt<S::kLoadsPerStage>();
+      else wait_vmcnt<0>();
+      // Bare s_barrier: this wave's DMA for stage st has landed (vmcnt above), and
+      // its reads of stage st-1's buffer were consumed in the previous iteration.
+      // __syncthreads() would also wait for every DMA still in flight.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (st + NS - 1 < nst) issue(st + NS - 1);
+      const unsigned char* base = smem + (int)(st % NS) * S::kStage;
       // this lane's operand words of stage st: code fragments [q][i] (A) and
       // [q][j] (B), 16 B each, and one scale word per fragment row
       u32x4_t fa[2][WM], fb[2][WN];
@@ -549,281 +632,59 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     }
     __syncthreads();
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
+    // v[16 i + q]: this lane's sum of f^2 over its WN columns of row (i, q)
+    constexpr int NV = WM * 16;
+    static_assert(NV % 32 == 0, "row partials must split evenly over 32 lanes");
+    float v[NV];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * 32 * WM + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3);
-        float ss = 0.0f;
-        const bool ok = row < rows_here;
-        const int64_t p = prow[row];
-        const float wp = wrow[row];
+      for (int qh = 0; qh < 4; ++qh) {
+        // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
+        const int rb = wm * 32 * WM + 32 * i + 8 * qh + 4 * g;
+        const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
+        const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
 #pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const float f = acc[i][j][q] * alpha;
-          ss += f * f;
-          if (ok) a.pair_out[p * a.H + (int64_t)nt * BN + wn * 32 * WN + 32 * j + r] = wp * f;
+        for (int qq = 0; qq < 4; ++qq) {
+          const int q = 4 * qh + qq, row = rb + qq;
+          const bool ok = row < rows_here;
+          const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
+          const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
+          float ss = 0.0f;
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const float f = acc[i][j][q] * alpha;
+            ss += f * f;
+            if (ok) a.pair_out[p * a.H + (int64_t)nt * BN + wn * 32 * WN + 32 * j + r] = wp * f;
+          }
+          v[16 * i + q] = ss;
         }
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 32);
-        if (r == 0) sqbuf[wn * BM + row] = ss;
       }
+    }
+    // Sum each row's partials over the 32 lanes of the half-wave with a
+    // transposed butterfly: at each level a lane keeps half of its remaining
+    // rows and sends the other half to its partner (lane ^ mask), so the
+    // shuffles of a level are independent.  Afterwards lane r holds the sums of
+    // rows 16 i + q = (NV / 32) r + k.  The order is fixed: deterministic.
+#pragma unroll
+    for (int lvl = 0; lvl < 5; ++lvl) {
+      const int mask = 16 >> lvl, half = (NV >> lvl) / 2;
+      const bool up = (r & mask) != 0;
+#pragma unroll
+      for (int k = 0; k < half; ++k) {
+        const float send = up ? v[k] : v[k + half];
+        const float keep = up ? v[k + half] : v[k];
+        v[k] = keep + __shfl_xor(send, mask, 32);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NV / 32; ++k) {
+      const int idx = (NV / 32) * r + k, i = idx >> 4, q = idx & 15;
+      sqbuf[wn * BM + wm * 32 * WM + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[k];
     }
     __syncthreads();
     if (a.sq_part != nullptr && tid < BM && tid < rows_here)
       a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = sqbuf[tid] + sqbuf[BM + tid];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// tiled kernel, eight waves: two per SIMD
-//
-// Same 256 x 256 workgroup tile, LDS layout and 4-stage DMA ring as above, but
-// eight waves in a 2 (M) x 4 (N) grid, each owning 128 x 64 of the tile (4 x 2
-// accumulators of 32 x 32, 128 registers), so two waves share each SIMD and
-// one wave's decode can run beside the other's MFMAs.  Each A fragment is then
-// decoded by four waves instead of two (1.5x the decode work per MFMA); the
-// launcher picks the variant per stage from measurements.
-
-namespace t8 {
-constexpr int BM = 256, BN = 256, NS = 4, kWaves = 8;
-constexpr int kACodeBytes = BM * 64, kAScaleBytes = BM * 8, kBCodeBytes = BN * 64, kBScaleBytes = BN * 8;
-constexpr int kStage = kACodeBytes + kAScaleBytes + kBCodeBytes + kBScaleBytes;
-constexpr int kHcols = 128;            // gate_up: h columns per tile (each wave: 32 gate + 32 up columns)
-constexpr int kHStride = kHcols + 4;   // floats per LDS row of h
-constexpr int kHBytes = BM * kHStride * 4;
-constexpr int kSqBytes = 4 * BM * 4;   // down: one sum of squares per (N wave, row)
-constexpr int kLds = (NS * kStage > kHBytes ? NS * kStage : kHBytes) + kSqBytes;
-// DMA instructions per wave per stage: 16-byte code loads cover 16 rows (16 per operand
-// over 8 waves), 4-byte scale loads cover 32 rows (8 per operand)
-constexpr int kLoadsPerStage = 2 + 1 + 2 + 1;
-}  // namespace t8
-
-template <int MODE>
-__global__ __launch_bounds__(512) void ffn_tiled8_kernel(FfnArgs a) {
-  using namespace t8;
-  const int nt = blockIdx.x;
-  const int mt = blockIdx.y;
-  if (mt >= a.num_tiles[0]) return;
-  const int e = a.tile_expert[mt];
-  const int row0 = a.tile_row0[mt];
-  const int off = a.offsets[e];
-  const int rows_here = min(BM, a.offsets[e + 1] - off - row0);
-
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  const int r = lane & 31, g = lane >> 5;
-  const int64_t K = a.K, kbytes = K / 2, kscales = K / 16;
-
-  // Rows past rows_here read the tile's first row; their outputs are never stored.
-  auto a_row = [&](int m) -> int64_t {
-    const int mm = m < rows_here ? m : 0;
-    return (MODE == kGateUp) ? (int64_t)(a.sorted[off + row0 + mm] / a.k) : (int64_t)(off + row0 + mm);
-  };
-  // B tile row n: N wave n / 64 owns h columns nt*128 + 32*(n/64) + 0..31, as gate rows
-  // (n % 64 < 32) and as up rows (n % 64 >= 32)
-  auto b_row = [&](int n) -> int64_t {
-    if (MODE == kGateUp) {
-      const int wv = n >> 6, j = (n >> 5) & 1, cc = n & 31;
-      return (int64_t)e * 2 * a.I + (j ? a.I : 0) + (int64_t)nt * kHcols + 32 * wv + cc;
-    }
-    return (int64_t)e * a.H + (int64_t)nt * BN + n;
-  };
-  const int64_t erow0 = MODE == kGateUp ? (int64_t)e * 2 * a.I : (int64_t)e * a.H;
-  const uint8_t* b_code_expert = a.b_codes + erow0 * kbytes;
-  const uint8_t* b_scale_expert = a.b_scales + (erow0 >> 4) * K;
-  // 16-byte code DMA i (0, 1) of this wave: rows 16 q .. 16 q + 15, q = 8 i + wave; lane -> row
-  // 16 q + lane / 4, LDS slot lane % 4 holding chunk slot ^ ((row >> 2) & 3)
-  uint32_t a_code_off[2], b_code_off[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 16 * (8 * i + wave) + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    a_code_off[i] = (uint32_t)(a_row(row) * kbytes) + 16 * chunk;
-    b_code_off[i] = (uint32_t)((b_row(row) - erow0) * kbytes) + 16 * chunk;
-  }
-  // 4-byte scale DMA of this wave: rows 32 wave .. 32 wave + 31; lane -> row 32 wave + lane / 2, dword lane % 2
-  const int srow = 32 * wave + (lane >> 1);
-  const uint32_t a_scale_off = (uint32_t)(a_row(srow) * kscales) + 4 * (lane & 1);
-  const uint32_t b_scale_off = (uint32_t)tiled_scale_index(b_row(srow) - erow0, 0, K) + 4 * (lane & 1);
-
-  auto issue = [&](int64_t st) {
-    unsigned char* base = smem + (int)(st % NS) * kStage;
-    const uint8_t* ac = a.a_codes + st * 64;  // 128 k per stage
-    const uint8_t* as = a.a_scales + st * 8;
-    const uint8_t* bc = b_code_expert + st * 64;
-    const uint8_t* bs = b_scale_expert + st * 128;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(ac + a_code_off[i], base + (8 * i + wave) * 1024);
-    dma4(as + a_scale_off, base + kACodeBytes + wave * 256);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(bc + b_code_off[i], base + kACodeBytes + kAScaleBytes + (8 * i + wave) * 1024);
-    dma4(bs + b_scale_off, base + kACodeBytes + kAScaleBytes + kBCodeBytes + wave * 256);
-  };
-
-  float16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  const uint32_t a_lane = (uint32_t)(wm * 128 + r) * 64u;
-  const uint32_t b_lane = (uint32_t)(kACodeBytes + kAScaleBytes) + (uint32_t)(wn * 64 + r) * 64u;
-  const uint32_t as_lane = (uint32_t)kACodeBytes + (uint32_t)(wm * 128 + r) * 8u + 4u * g;
-  const uint32_t bs_lane = (uint32_t)(kACodeBytes + kAScaleBytes + kBCodeBytes) + (uint32_t)(wn * 64 + r) * 8u + 4u * g;
-  const uint32_t slot_q0 = (uint32_t)((2 * g) ^ ((r >> 2) & 3)), slot_q1 = (uint32_t)((2 * g + 1) ^ ((r >> 2) & 3));
-
-  const int64_t nst = K / 128;
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nst) issue(p);
-  for (int64_t st = 0; st < nst; ++st) {
-    const int64_t ahead = nst - 1 - st;
-    if (ahead >= NS - 2) wait_vmcnt<kLoadsPerStage * (NS - 2)>();
-    else if (ahead == 1) wait_vmcnt<kLoadsPerStage>();
-    else wait_vmcnt<0>();
-    // bare s_barrier: every wave's DMA for stage st has landed, and the reads of stage st-1's
-    // buffer are done (they ended in lgkmcnt(0) waits)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const uint32_t sb = lds_base + (uint32_t)(st % NS) * kStage;
-    const uint32_t a0 = sb + a_lane + 16u * slot_q0, a1 = sb + a_lane + 16u * slot_q1;
-    const uint32_t b0 = sb + b_lane + 16u * slot_q0, b1 = sb + b_lane + 16u * slot_q1;
-    const uint32_t as_addr = sb + as_lane, bs_addr = sb + bs_lane;
-    // fragment i of the wave's A rows sits 2048 B (32 rows) after fragment i-1, its scale word 256 B after
-    u32x4_t fa[4], fb[2];
-    uint32_t sa[4], sbv[2];
-    asm volatile(
-        "ds_read_b32 %6, %14 offset:0\n"
-        "ds_read_b32 %7, %14 offset:256\n"
-        "ds_read_b32 %8, %14 offset:512\n"
-        "ds_read_b32 %9, %14 offset:768\n"
-        "ds_read_b32 %10, %15 offset:0\n"
-        "ds_read_b32 %11, %15 offset:256\n"
-        "ds_read_b128 %0, %12 offset:0\n"
-        "ds_read_b128 %1, %12 offset:2048\n"
-        "ds_read_b128 %2, %12 offset:4096\n"
-        "ds_read_b128 %3, %12 offset:6144\n"
-        "ds_read_b128 %4, %13 offset:0\n"
-        "ds_read_b128 %5, %13 offset:2048\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]), "=&v"(sa[0]),
-          "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sbv[0]), "=&v"(sbv[1])
-        : "v"(a0), "v"(b0), "v"(as_addr), "v"(bs_addr)
-        : "memory");
-    half8_t da[2][4], db[2][2];
-    auto decode_step = [&](int ss, int buf) {
-      const int sbyte = 2 * (ss >> 2) + ((ss & 3) >> 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][ss & 3], scale_pair(sa[i], sbyte));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) db[buf][j] = decode8(fb[j][ss & 3], scale_pair(sbv[j], sbyte));
-    };
-    decode_step(0, 0);
-#pragma unroll
-    for (int ss = 0; ss < 8; ++ss) {
-      const int cur = ss & 1;
-      if (ss == 3) {
-        asm volatile(
-            "ds_read_b128 %0, %6 offset:0\n"
-            "ds_read_b128 %1, %6 offset:2048\n"
-            "ds_read_b128 %2, %6 offset:4096\n"
-            "ds_read_b128 %3, %6 offset:6144\n"
-            "ds_read_b128 %4, %7 offset:0\n"
-            "ds_read_b128 %5, %7 offset:2048\n"
-            "s_waitcnt lgkmcnt(0)\n"
-            : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1])
-            : "v"(a1), "v"(b1)
-            : "memory");
-      }
-      if (ss + 1 < 8) decode_step(ss + 1, cur ^ 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[cur][i], db[cur][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-    }
-  }
-  __syncthreads();  // every wave is done with the ring before the epilogue reuses the LDS
-
-  // ---- epilogues.  acc[i][j][q]: row wm*128 + 32 i + 8 (q/4) + 4 g + q%4, column r of B fragment j
-  if (MODE == kGateUp) {
-    float* hbuf = reinterpret_cast<float*>(smem);
-    const float alpha_g = 1.0f / (a.a_gs[0] * a.b_gs[2 * e]);
-    const float alpha_u = 1.0f / (a.a_gs[0] * a.b_gs[2 * e + 1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * 128 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3);
-        const float gv = acc[i][0][q] * alpha_g;
-        const float uv = acc[i][1][q] * alpha_u;
-        hbuf[row * kHStride + wn * 32 + r] = silu(gv) * uv;
-      }
-    __syncthreads();
-    const float gsh = a.h_gs[e];
-    constexpr int kBlkPerRow = kHcols / 16;
-    for (int b = tid; b < BM * kBlkPerRow; b += 512) {
-      const int row = b / kBlkPerRow, cb = b % kBlkPerRow;
-      if (row >= rows_here) continue;
-      float h[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) h[i] = hbuf[row * kHStride + 16 * cb + i];
-      uint32_t lo, hi;
-      const uint32_t sc = quantize_block16(h, gsh, lo, hi);
-      const int64_t hrow = off + row0 + row;
-      const int64_t hcol = (int64_t)nt * kHcols + 16 * cb;
-      *reinterpret_cast<uint2*>(a.h_codes + hrow * (a.I / 2) + hcol / 2) = make_uint2(lo, hi);
-      a.h_scales[hrow * (a.I / 16) + hcol / 16] = (uint8_t)sc;
-    }
-  } else {
-    float* sqbuf = reinterpret_cast<float*>(smem + (kLds - kSqBytes));
-    // the tile's pair ids and weights, staged once in the (now free) ring
-    int32_t* prow = reinterpret_cast<int32_t*>(smem);
-    float* wrow = reinterpret_cast<float*>(smem + BM * 4);
-    for (int t = tid; t < BM; t += 512) {
-      const int32_t p = t < rows_here ? a.sorted[off + row0 + t] : 0;
-      prow[t] = p;
-      wrow[t] = t < rows_here ? a.topk_w[p] : 0.0f;
-    }
-    __syncthreads();
-    const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = wm * 128 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3);
-        float ss = 0.0f;
-        const bool ok = row < rows_here;
-        const int64_t p = prow[row];
-        const float wp = wrow[row];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float f = acc[i][j][q] * alpha;
-          ss += f * f;
-          if (ok) a.pair_out[p * a.H + (int64_t)nt * BN + wn * 64 + 32 * j + r] = wp * f;
-        }
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 32);
-        if (r == 0) sqbuf[wn * BM + row] = ss;
-      }
-    }
-    __syncthreads();
-    if (a.sq_part != nullptr && tid < BM && tid < rows_here)
-      a.sq_part[(int64_t)prow[tid] * a.n_part + nt] =
-          ((sqbuf[tid] + sqbuf[BM + tid]) + sqbuf[2 * BM + tid]) + sqbuf[3 * BM + tid];
   }
 }
 
@@ -880,9 +741,6 @@ __global__ void sq_reduce_kernel(const float* __restrict__ part, int64_t npairs,
 #ifndef MOE_TILED_NS
 #define MOE_TILED_NS 4
 #endif
-#ifndef MOE_TILED_DOWN_WAVES
-#define MOE_TILED_DOWN_WAVES 8  // down stage: 8 = ffn_tiled8_kernel, 4 = ffn_tiled_kernel
-#endif
 constexpr int kTiledWM = MOE_TILED_WM, kTiledWN = MOE_TILED_WN, kTiledNS = MOE_TILED_NS;
 using Tiled = TiledShape<kTiledWM, kTiledWN, kTiledNS>;
 
@@ -910,7 +768,6 @@ hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool buil
                        const_cast<int32_t*>(a.num_tiles));
   }
   const unsigned gy = (unsigned)ffn_max_tiles(T, a.k, E);
-  static_assert(t8::BM == Tiled::BM && t8::BN == Tiled::BN && t8::kHcols == Tiled::kHcols, "tile shapes");
   // the tiles need more than the default 64 KiB of dynamic LDS
   if (hipError_t e = set_max_dynamic_lds(
           reinterpret_cast<const void*>(&ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>), Tiled::kLds))
@@ -918,15 +775,10 @@ hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool buil
   if (hipError_t e = set_max_dynamic_lds(
           reinterpret_cast<const void*>(&ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>), Tiled::kLds))
     return e;
-  if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ffn_tiled8_kernel<kDown>), t8::kLds)) return e;
   if (mode == kGateUp) {
-    // four waves (measured on the 8192-token Zipf prefill: 3.08 ms against 3.20 ms with eight)
     const unsigned gx = (unsigned)(a.I / Tiled::kHcols);
     hipLaunchKernelGGL((ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>), dim3(gx, gy), dim3(256), Tiled::kLds,
                        st, a);
-  } else if (MOE_TILED_DOWN_WAVES == 8) {
-    // eight waves (same workload: 2.13 ms against 2.18 ms with four)
-    hipLaunchKernelGGL(ffn_tiled8_kernel<kDown>, dim3((unsigned)(a.H / t8::BN), gy), dim3(512), t8::kLds, st, a);
   } else {
     const unsigned gx = (unsigned)(a.H / Tiled::BN);
     hipLaunchKernelGGL((ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>), dim3(gx, gy), dim3(256), Tiled::kLds, st,
