@@ -276,6 +276,7 @@ def test_layer_parity_config0(ops):
     ("k_equals_e", 17, 256, 128, 4, 4),
     ("many_empty_experts", 40, 256, 128, 256, 8),
     ("tiled_mid", 130, 768, 384, 6, 3),
+    ("tiled_k5", 40, 512, 640, 4, 2),  # down K = 640: five ring stages (one past the ring depth)
     ("stream_decode", 12, 2048, 2048, 8, 2),  # persistent decode kernel: K >= 2048, K % 1024 == 0
     ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: three K steps per wave and item
 ])
