@@ -233,47 +233,64 @@ void ffn_small_kernel(FfnArgs a) {
 
 // ---------------------------------------------------------------------------
 // tiled kernel
+//
+// Four waves, each owning a 128 x 128 block of 16 accumulator tiles.  A full
+// tile is 256 pair rows x 256 weight rows (waves 2 x 2).  An expert's last
+// m-tile with at most 128 rows is run wide instead: 128 pair rows x 512 weight
+// rows (n-tiles nt and nt + gx / 2, waves 1 x 4 over the weight rows), and the
+// workgroups of the second half of the n-tiles exit, so no MFMA work goes to
+// the empty half.  Pairing nt with nt + gx / 2 rather than nt + 1 keeps the
+// running workgroups spread over all XCDs (workgroups go to the XCDs in turn
+// by linear id).
 
-template <int WM, int WN, int NS>
-struct TiledShape {
-  static constexpr int BM = 64 * WM;  // 2 waves in M, WM 32-row MFMA tiles each
-  static constexpr int BN = 64 * WN;  // 2 waves in N, WN 32-col MFMA tiles each
+template <bool WIDE>
+struct TileShape {
+  static constexpr int kARows = WIDE ? 128 : 256;  // pair rows (A)
+  static constexpr int kBRows = WIDE ? 512 : 256;  // weight rows (B)
+  static constexpr int NS = WIDE ? 3 : 4;          // ring stages of 128 k
   // codes: [row][4 slots of 16 B], chunk c of row r in slot c ^ ((r >> 2) & 3):
   // 16 lanes reading one chunk of 16 consecutive rows, and the 16 lanes of a
   // DMA group writing the 4 chunks of 4 consecutive rows, each touch 16
   // distinct 16-byte bank groups (64 banks); scales: [row][8 B]
-  static constexpr int kACodeBytes = BM * 64;
-  static constexpr int kAScaleBytes = BM * 8;
-  static constexpr int kBCodeBytes = BN * 64;
-  static constexpr int kBScaleBytes = BN * 8;
+  static constexpr int kACodeBytes = kARows * 64;
+  static constexpr int kAScaleBytes = kARows * 8;
+  static constexpr int kBCodeBytes = kBRows * 64;
+  static constexpr int kBScaleBytes = kBRows * 8;
   static constexpr int kStage = kACodeBytes + kAScaleBytes + kBCodeBytes + kBScaleBytes;
-  static constexpr int kHcols = BN / 2;             // gate_up: h columns per tile
-  static constexpr int kHStride = kHcols + 4;       // floats per LDS row of h
-  static constexpr int kHBytes = BM * kHStride * 4;
-  static constexpr int kLds = (NS * kStage > kHBytes ? NS * kStage : kHBytes) + 2 * BM * 4;
-  // DMA instructions per wave per stage (4 waves): 16-byte code loads cover 16
-  // rows, 4-byte scale loads cover 32 rows
-  static constexpr int kACodeOps = BM / 64, kAScaleOps = BM / 128;
-  static constexpr int kBCodeOps = BN / 64, kBScaleOps = BN / 128;
+  static constexpr int kHcols = kBRows / 2;     // gate_up: h columns per tile
+  static constexpr int kHStride = kHcols + 4;   // floats per LDS row of h
+  static constexpr int kHBytes = kARows * kHStride * 4;
+  static constexpr int kBody = NS * kStage > kHBytes ? NS * kStage : kHBytes;
+  // DMA instructions per wave per stage: 16-byte code loads cover 16 rows,
+  // 4-byte scale loads cover 32 rows
+  static constexpr int kACodeOps = kARows / 64, kAScaleOps = kARows / 128;
+  static constexpr int kBCodeOps = kBRows / 64, kBScaleOps = kBRows / 128;
   static constexpr int kLoadsPerStage = kACodeOps + kAScaleOps + kBCodeOps + kBScaleOps;
 };
+struct Tiled {
+  static constexpr int BM = 256, BN = 256, kHcols = 128;  // the full tile: m-tile height, n-tile width
+  static constexpr int kSqBytes = 2 * 2 * 128 * 4;          // down: Σf² partials [n-tile half][wn][row]
+  static constexpr int kLds =
+      (TileShape<false>::kBody > TileShape<true>::kBody ? TileShape<false>::kBody : TileShape<true>::kBody) + kSqBytes;
+};
+static_assert(TileShape<false>::kHcols == Tiled::kHcols && TileShape<false>::kBRows == Tiled::BN &&
+                  TileShape<false>::kARows == Tiled::BM, "full tile shape");
+static_assert(Tiled::kLds <= 160 * 1024, "LDS");
 
-template <int MODE, int WM, int WN, int NS>
-__global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
-  using S = TiledShape<WM, WN, NS>;
-  constexpr int BM = S::BM, BN = S::BN;
-  const int nt = blockIdx.x;
-  const int mt = blockIdx.y;
-  if (mt >= a.num_tiles[0]) return;
-  const int e = a.tile_expert[mt];
-  const int row0 = a.tile_row0[mt];
-  const int off = a.offsets[e];
-  const int rows_here = min(BM, a.offsets[e + 1] - off - row0);
-
+// One tile: rows row0 .. row0 + rows_here - 1 of expert e's pairs against
+// n-tile nt (and nt2 when WIDE).
+template <int MODE, bool WIDE>
+__device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, int e, int row0, int off,
+                                           int rows_here) {
+  using S = TileShape<WIDE>;
+  constexpr int NS = S::NS;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
+  // this wave's first A row and first B row inside the tile
+  const int a_row0 = WIDE ? 0 : 128 * wm;
+  const int b_row0 = WIDE ? 256 * wm + 128 * wn : 128 * wn;
   const int64_t K = a.K, kbytes = K / 2, kscales = K / 16;
 
   // ---- per-lane DMA sources.  Rows past rows_here read the tile's first row:
@@ -282,13 +299,18 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     const int mm = m < rows_here ? m : 0;
     return (MODE == kGateUp) ? (int64_t)(a.sorted[off + row0 + mm] / a.k) : (int64_t)(off + row0 + mm);
   };
+  // B rows 0..255 belong to n-tile nt, rows 256..511 (WIDE) to n-tile nt2.
+  // gate_up: each 128-row wave block holds 64 gate rows then the 64 up rows of
+  // the same h columns (so SwiGLU pairs meet in one wave's registers)
   auto b_row = [&](int n) -> int64_t {
+    const int64_t ntile = n < 256 ? nt : nt2;
+    const int nl = n % 256;
     if (MODE == kGateUp) {
-      const int wv = n / (32 * WN), j = (n % (32 * WN)) / 32, cc = n % 32;
-      const int64_t col = (int64_t)nt * S::kHcols + wv * 16 * WN + 32 * (j % (WN / 2)) + cc;
-      return (int64_t)e * 2 * a.I + (j < WN / 2 ? 0 : a.I) + col;
+      const int wv = nl / 128, j = (nl % 128) / 32, cc = nl % 32;
+      const int64_t col = ntile * Tiled::kHcols + wv * 64 + 32 * (j % 2) + cc;
+      return (int64_t)e * 2 * a.I + (j < 2 ? 0 : a.I) + col;
     } else {
-      return (int64_t)e * a.H + (int64_t)nt * BN + n;
+      return (int64_t)e * a.H + ntile * Tiled::BN + nl;
     }
   };
   // DMA sources: a wave-uniform base per operand that advances with the stage
@@ -325,289 +347,210 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     b_scale_off[i] = (uint32_t)tiled_scale_index(br, 0, K) + 4 * (lane & 1);  // tiled: 128 B per stage
   }
 
-  auto issue = [&](int64_t st) {
-    unsigned char* base = smem + (int)(st % NS) * S::kStage;
+  float16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  // this lane's LDS byte offsets inside a stage
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  const uint32_t a_lane = (uint32_t)(a_row0 + r) * 64u;
+  const uint32_t b_lane = (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (uint32_t)(b_row0 + r) * 64u;
+  const uint32_t as_lane = (uint32_t)S::kACodeBytes + (uint32_t)(a_row0 + r) * 8u + 4u * g;
+  const uint32_t bs_lane =
+      (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (uint32_t)(b_row0 + r) * 8u + 4u * g;
+  // rows read by this lane are r + multiples of 32, so (row >> 2) & 3 == (r >> 2) & 3
+  const uint32_t slot_q0 = (uint32_t)((2 * g) ^ ((r >> 2) & 3)), slot_q1 = (uint32_t)((2 * g + 1) ^ ((r >> 2) & 3));
+
+  // Pipelined ring.  The DMA is issued as inline asm, so the compiler issues
+  // the fragment reads itself, with per-read lgkmcnt waits, and never drains
+  // the DMA still in flight.  Each 128-k stage is two halves of four 16-k
+  // sub-steps: the second half's code words are read during the first half,
+  // and after the one barrier per stage (mid-stage) the next stage's
+  // first-half words and scales are read during the second half.  The decode
+  // of sub-step n + 1 runs beside the 16 MFMAs of sub-step n throughout,
+  // across stage boundaries too.
+  //
+  // Ring: the prologue fills all NS slots.  At the mid-stage barrier of stage
+  // st every wave has finished its reads of slot st % NS (lgkmcnt(0) before
+  // the barrier) and waited for its DMA of stage st + 1, so stage st + NS is
+  // issued into slot st % NS right after it.
+  const int64_t nst = K / 128;
+  constexpr int L = S::kLoadsPerStage;
+  static_assert((NS - 1) * L < 64, "vmcnt range");
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
+  auto issue_async = [&](int64_t st) {
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(st % NS) * (uint32_t)S::kStage);
     const uint8_t* ac = a.a_codes + st * 64;  // 128 k per stage
     const uint8_t* as = a.a_scales + st * 8;
     const uint8_t* bc = b_code_expert + st * 64;
     const uint8_t* bs = b_scale_expert + st * 128;
 #pragma unroll
-    for (int i = 0; i < S::kACodeOps; ++i) dma16(ac + a_code_off[i], base + (4 * i + wave) * 1024);
+    for (int i = 0; i < S::kACodeOps; ++i) dma16_async(ac, a_code_off[i], sb + (4 * i + wave_u) * 1024u);
 #pragma unroll
-    for (int i = 0; i < S::kAScaleOps; ++i) dma4(as + a_scale_off[i], base + S::kACodeBytes + (4 * i + wave) * 256);
+    for (int i = 0; i < S::kAScaleOps; ++i)
+      dma4_async(as, a_scale_off[i], sb + (uint32_t)S::kACodeBytes + (4 * i + wave_u) * 256u);
 #pragma unroll
     for (int i = 0; i < S::kBCodeOps; ++i)
-      dma16(bc + b_code_off[i], base + S::kACodeBytes + S::kAScaleBytes + (4 * i + wave) * 1024);
+      dma16_async(bc, b_code_off[i], sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (4 * i + wave_u) * 1024u);
 #pragma unroll
     for (int i = 0; i < S::kBScaleOps; ++i)
-      dma4(bs + b_scale_off[i], base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes + (4 * i + wave) * 256);
+      dma4_async(bs, b_scale_off[i],
+                 sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (4 * i + wave_u) * 256u);
   };
-
-  float16_t acc[WM][WN];
+  // this lane's fragment words of one half (fragment i of a row block sits
+  // 2048 B = 32 rows after fragment i-1) and its scale words (256 B apart)
+  auto load_half = [&](int64_t st, uint32_t slot, u32x4_t* fa, u32x4_t* fb) {
+    const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < 4; ++i)
+      fa[i] = *reinterpret_cast<const u32x4_t*>(smem + sb + a_lane + 16u * slot + 2048u * i);
 #pragma unroll
-    for (int j = 0; j < WN; ++j)
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const u32x4_t*>(smem + sb + b_lane + 16u * slot + 2048u * j);
+  };
+  auto load_scales = [&](int64_t st, uint32_t* sa, uint32_t* sbv) {
+    const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  // LDS byte addresses used by the asm fragment reads (see the loop)
-  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  const uint32_t a_lane = (uint32_t)(wm * 32 * WM + r) * 64u;
-  const uint32_t b_lane = (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (uint32_t)(wn * 32 * WN + r) * 64u;
-  const uint32_t as_lane = (uint32_t)S::kACodeBytes + (uint32_t)(wm * 32 * WM + r) * 8u + 4u * g;
-  const uint32_t bs_lane =
-      (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (uint32_t)(wn * 32 * WN + r) * 8u + 4u * g;
-  const uint32_t slot_q0 = (uint32_t)((2 * g) ^ ((r >> 2) & 3)), slot_q1 = (uint32_t)((2 * g + 1) ^ ((r >> 2) & 3));
-  (void)lds_base; (void)a_lane; (void)b_lane; (void)as_lane; (void)bs_lane; (void)slot_q0; (void)slot_q1;
-
-  const int64_t nst = K / 128;
-  if constexpr (WM == 4 && WN == 4) {
-    // Pipelined ring.  The DMA is issued as inline asm, so the compiler issues
-    // the fragment reads itself, with per-read lgkmcnt waits, and never drains
-    // the DMA still in flight.  Each 128-k stage is two halves of four 16-k
-    // sub-steps: the second half's code words are read during the first half,
-    // and after the one barrier per stage (mid-stage) the next stage's
-    // first-half words and scales are read during the second half.  The decode
-    // of sub-step n + 1 runs beside the 16 MFMAs of sub-step n throughout,
-    // across stage boundaries too.
-    //
-    // Ring: the prologue fills all NS slots.  At the mid-stage barrier of stage
-    // st every wave has finished its reads of slot st % NS (lgkmcnt(0) before
-    // the barrier) and waited for its DMA of stage st + 1, so stage st + NS is
-    // issued into slot st % NS right after it.
-    constexpr int L = S::kLoadsPerStage;
-    const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
-    auto issue_async = [&](int64_t st) {
-      const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(st % NS) * (uint32_t)S::kStage);
-      const uint8_t* ac = a.a_codes + st * 64;  // 128 k per stage
-      const uint8_t* as = a.a_scales + st * 8;
-      const uint8_t* bc = b_code_expert + st * 64;
-      const uint8_t* bs = b_scale_expert + st * 128;
+    for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(smem + sb + as_lane + 256u * i);
 #pragma unroll
-      for (int i = 0; i < S::kACodeOps; ++i) dma16_async(ac, a_code_off[i], sb + (4 * i + wave_u) * 1024u);
+    for (int j = 0; j < 4; ++j) sbv[j] = *reinterpret_cast<const uint32_t*>(smem + sb + bs_lane + 256u * j);
+  };
+  // sub-step ss (q = ss / 4 half, dword ss % 4) uses scale byte 2 q + (ss % 4) / 2 of the lane's word
+  half8_t da[2][4], db[2][4];
+  auto decode = [&](int buf, const u32x4_t* fa, const u32x4_t* fb, int w, const uint32_t* sa, const uint32_t* sbv,
+                    int sbyte) {
 #pragma unroll
-      for (int i = 0; i < S::kAScaleOps; ++i)
-        dma4_async(as, a_scale_off[i], sb + (uint32_t)S::kACodeBytes + (4 * i + wave_u) * 256u);
+    for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][w], scale_pair(sa[i], sbyte));
 #pragma unroll
-      for (int i = 0; i < S::kBCodeOps; ++i)
-        dma16_async(bc, b_code_off[i], sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (4 * i + wave_u) * 1024u);
+    for (int j = 0; j < 4; ++j) db[buf][j] = decode8(fb[j][w], scale_pair(sbv[j], sbyte));
+  };
+  // the 16 MFMAs of a sub-step, each followed by a slice of the next
+  // sub-step's decode and, for the first n_ds, by one of the LDS reads just
+  // issued in program order (so they go out early instead of just before use)
+  auto mfma16 = [&](int buf, int n_ds) {
 #pragma unroll
-      for (int i = 0; i < S::kBScaleOps; ++i)
-        dma4_async(bs, b_scale_off[i],
-                   sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (4 * i + wave_u) * 256u);
-    };
-    // this lane's fragment words of one half (fragment i of a row block sits
-    // 2048 B = 32 rows after fragment i-1) and its scale words (256 B apart)
-    auto load_half = [&](int64_t st, uint32_t slot, u32x4_t* fa, u32x4_t* fb) {
-      const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const u32x4_t*>(smem + sb + a_lane + 16u * slot + 2048u * i);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const u32x4_t*>(smem + sb + b_lane + 16u * slot + 2048u * j);
-    };
-    auto load_scales = [&](int64_t st, uint32_t* sa, uint32_t* sbv) {
-      const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[buf][i], db[buf][j], acc[i][j], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(smem + sb + as_lane + 256u * i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sbv[j] = *reinterpret_cast<const uint32_t*>(smem + sb + bs_lane + 256u * j);
-    };
-    // sub-step ss (q = ss / 4 half, dword ss % 4) uses scale byte 2 q + (ss % 4) / 2 of the lane's word
-    half8_t da[2][4], db[2][4];
-    auto decode = [&](int buf, const u32x4_t* fa, const u32x4_t* fb, int w, const uint32_t* sa, const uint32_t* sbv,
-                      int sbyte) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][w], scale_pair(sa[i], sbyte));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) db[buf][j] = decode8(fb[j][w], scale_pair(sbv[j], sbyte));
-    };
-    // the 16 MFMAs of a sub-step, each followed by a slice of the next
-    // sub-step's decode and, for the first n_ds, by one of the LDS reads just
-    // issued in program order (so they go out early instead of just before use)
-    auto mfma16 = [&](int buf, int n_ds) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[buf][i], db[buf][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (m < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-    };
+    for (int m = 0; m < 16; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (m < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
+  };
 
 #pragma unroll
-    for (int p = 0; p < NS; ++p)
-      if (p < nst) issue_async(p);
-    // stage 0 has landed; up to NS - 1 later stages may stay in flight
-    if (nst >= 4) wait_vmcnt<3 * L>();
-    else if (nst == 3) wait_vmcnt<2 * L>();
-    else if (nst == 2) wait_vmcnt<L>();
+  for (int p = 0; p < NS; ++p)
+    if (p < nst) issue_async(p);
+  // stage 0 has landed; up to NS - 1 later stages may stay in flight
+  {
+    const int64_t later = nst - 1 < NS - 1 ? nst - 1 : NS - 1;
+    if (later >= 3) wait_vmcnt<3 * L>();
+    else if (later == 2) wait_vmcnt<2 * L>();
+    else if (later == 1) wait_vmcnt<L>();
     else wait_vmcnt<0>();
-    barrier_after_lds();
-    u32x4_t c0a[4], c0b[4];
-    uint32_t sa[4], sbv[4];
-    load_half(0, slot_q0, c0a, c0b);
-    load_scales(0, sa, sbv);
-    decode(0, c0a, c0b, 0, sa, sbv, 0);
-    // One stage; MORE: a stage follows, ISSUE: stage st + NS exists.  The
-    // loop is peeled on both so the steady-state body has no branch, and the
-    // compiler's LDS wait counts stay exact.
-    auto stage = [&](int64_t st, auto more_c, auto issue_c) {
-      constexpr bool kMore = decltype(more_c)::value, kIssue = decltype(issue_c)::value;
-      // Each sub-step is its own scheduling region (sched_barrier), so no
-      // decode, and no scale convert in particular, is hoisted next to the
-      // LDS read it depends on; the reads are issued at the top of a half.
-      u32x4_t c1a[4], c1b[4];
-      __builtin_amdgcn_sched_barrier(0);
-      load_half(st, slot_q1, c1a, c1b);
+  }
+  barrier_after_lds();
+  u32x4_t c0a[4], c0b[4];
+  uint32_t sa[4], sbv[4];
+  load_half(0, slot_q0, c0a, c0b);
+  load_scales(0, sa, sbv);
+  decode(0, c0a, c0b, 0, sa, sbv, 0);
+  // One stage; MORE: a stage follows, ISSUE: stage st + NS exists.  The
+  // loop is peeled on both so the steady-state body has no branch, and the
+  // compiler's LDS wait counts stay exact.
+  auto stage = [&](int64_t st, auto more_c, auto issue_c) {
+    constexpr bool kMore = decltype(more_c)::value, kIssue = decltype(issue_c)::value;
+    // Each sub-step is its own scheduling region (sched_barrier), so no
+    // decode, and no scale convert in particular, is hoisted next to the
+    // LDS read it depends on; the reads are issued at the top of a half.
+    u32x4_t c1a[4], c1b[4];
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(st, slot_q1, c1a, c1b);
 #pragma unroll
-      for (int ss = 0; ss < 4; ++ss) {
-        if (ss > 0) __builtin_amdgcn_sched_barrier(0);
-        if (ss < 3) decode((ss + 1) & 1, c0a, c0b, ss + 1, sa, sbv, (ss + 1) >> 1);
-        else decode(0, c1a, c1b, 0, sa, sbv, 2);
-        mfma16(ss & 1, ss == 0 ? 8 : 0);
-      }
-      u32x4_t n0a[4], n0b[4];
-      uint32_t nsa[4], nsb[4];
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kMore) {
-        // stage st + 1 has landed; the stages issued after it may stay in flight
-        if constexpr (kIssue) {
-          wait_vmcnt<2 * L>();
-        } else {
-          const int64_t ahead = nst - 2 - st;
-          if (ahead >= 2) wait_vmcnt<2 * L>();
-          else if (ahead == 1) wait_vmcnt<L>();
-          else wait_vmcnt<0>();
-        }
-        barrier_after_lds();
-        if constexpr (kIssue) issue_async(st + NS);
-        load_half(st + 1, slot_q0, n0a, n0b);
-        load_scales(st + 1, nsa, nsb);
-      }
+    for (int ss = 0; ss < 4; ++ss) {
+      if (ss > 0) __builtin_amdgcn_sched_barrier(0);
+      if (ss < 3) decode((ss + 1) & 1, c0a, c0b, ss + 1, sa, sbv, (ss + 1) >> 1);
+      else decode(0, c1a, c1b, 0, sa, sbv, 2);
+      mfma16(ss & 1, ss == 0 ? 8 : 0);
+    }
+    u32x4_t n0a[4], n0b[4];
+    uint32_t nsa[4], nsb[4];
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kMore) {
+      // stage st + 1 has landed; the stages issued after it (up to NS - 2) may stay in flight
+      const int64_t ahead = nst - 2 - st;
+      if (kIssue || ahead >= NS - 2) wait_vmcnt<(NS - 2) * L>();
+      else if (ahead == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+      barrier_after_lds();
+      if constexpr (kIssue) issue_async(st + NS);
+      load_half(st + 1, slot_q0, n0a, n0b);
+      load_scales(st + 1, nsa, nsb);
+    }
 #pragma unroll
-      for (int ss = 4; ss < 8; ++ss) {
-        if (ss > 4) __builtin_amdgcn_sched_barrier(0);
-        if (ss < 7) {
-          decode((ss + 1) & 1, c1a, c1b, (ss + 1) & 3, sa, sbv, 2 + (((ss + 1) & 3) >> 1));
-        } else if (kMore) {
-          // Pin the next stage's words here: instruction selection would
-          // otherwise place their (pure) converts right after the reads, and
-          // the wave would wait for the LDS there.
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            asm volatile("" : "+v"(nsa[i]), "+v"(nsb[i]));
-            asm volatile("" : "+v"(n0a[i]), "+v"(n0b[i]));
-          }
-          decode(0, n0a, n0b, 0, nsa, nsb, 0);
-        }
-        mfma16(ss & 1, (kMore && ss == 4) ? 12 : 0);
-      }
-      if constexpr (kMore) {
+    for (int ss = 4; ss < 8; ++ss) {
+      if (ss > 4) __builtin_amdgcn_sched_barrier(0);
+      if (ss < 7) {
+        decode((ss + 1) & 1, c1a, c1b, (ss + 1) & 3, sa, sbv, 2 + (((ss + 1) & 3) >> 1));
+      } else if (kMore) {
+        // Pin the next stage's words here: instruction selection would
+        // otherwise place their (pure) converts right after the reads, and
+        // the wave would wait for the LDS there.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          c0a[i] = n0a[i];
-          c0b[i] = n0b[i];
-          sa[i] = nsa[i];
-          sbv[i] = nsb[i];
+          asm volatile("" : "+v"(nsa[i]), "+v"(nsb[i]));
+          asm volatile("" : "+v"(n0a[i]), "+v"(n0b[i]));
         }
+        decode(0, n0a, n0b, 0, nsa, nsb, 0);
       }
-    };
-    int64_t st = 0;
-    for (; st + NS < nst; ++st) stage(st, std::true_type{}, std::true_type{});
-    for (; st + 1 < nst; ++st) stage(st, std::true_type{}, std::false_type{});
-    stage(st, std::false_type{}, std::false_type{});
-    wait_vmcnt<0>();  // nothing is in flight here; the epilogue's barrier does not know of the asm DMA
-  } else {
-    // NS-stage ring: stages st+1 .. st+NS-2 stay in flight while stage st is
-    // consumed; one barrier per stage both publishes stage st and frees the
-    // buffer of stage st-1 for the next DMA.
+      mfma16(ss & 1, (kMore && ss == 4) ? 12 : 0);
+    }
+    if constexpr (kMore) {
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < nst) issue(p);
-    for (int64_t st = 0; st < nst; ++st) {
-      const int64_t ahead = nst - 1 - st;  // stages issued after st that may still be in flight
-      if (ahead >= NS - 2) wait_vmcnt<S::kLoadsPerStage * (NS - 2)>();
-      else if (NS >= 4 && ahead == 2) wait_vmcnt<S::kLoadsPerStage * 2>();
-      else if (NS >= 3 && ahead == 1) wait_vmcnt<S::kLoadsPerStage>();
-      else wait_vmcnt<0>();
-      // Bare s_barrier: this wave's DMA for stage st has landed (vmcnt above), and
-      // its reads of stage st-1's buffer were consumed in the previous iteration.
-      // __syncthreads() would also wait for every DMA still in flight.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (st + NS - 1 < nst) issue(st + NS - 1);
-      const unsigned char* base = smem + (int)(st % NS) * S::kStage;
-      // this lane's operand words of stage st: code fragments [q][i] (A) and
-      // [q][j] (B), 16 B each, and one scale word per fragment row
-      u32x4_t fa[2][WM], fb[2][WN];
-      uint32_t sa[WM], sbv[WN];
-      const uint32_t* as = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes);
-      const uint32_t* bsc = reinterpret_cast<const uint32_t*>(base + S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes);
-      const u32x4_t* ac = reinterpret_cast<const u32x4_t*>(base);
-      const u32x4_t* bc = reinterpret_cast<const u32x4_t*>(base + S::kACodeBytes + S::kAScaleBytes);
-#pragma unroll
-      for (int i = 0; i < WM; ++i) sa[i] = as[(wm * 32 * WM + 32 * i + r) * 2 + g];
-#pragma unroll
-      for (int j = 0; j < WN; ++j) sbv[j] = bsc[(wn * 32 * WN + 32 * j + r) * 2 + g];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        // rows below are r + multiples of 32, so (row >> 2) & 3 == (r >> 2) & 3
-        const int slot = (2 * g + q) ^ ((r >> 2) & 3);
-#pragma unroll
-        for (int i = 0; i < WM; ++i) fa[q][i] = ac[(wm * 32 * WM + 32 * i + r) * 4 + slot];
-#pragma unroll
-        for (int j = 0; j < WN; ++j) fb[q][j] = bc[(wn * 32 * WN + 32 * j + r) * 4 + slot];
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int sbyte = 2 * q + (s >> 1);
-          half8_t af[WM], bf[WN];
-#pragma unroll
-          for (int i = 0; i < WM; ++i) af[i] = decode8(fa[q][i][s], scale_pair(sa[i], sbyte));
-#pragma unroll
-          for (int j = 0; j < WN; ++j) bf[j] = decode8(fb[q][j][s], scale_pair(sbv[j], sbyte));
-#pragma unroll
-          for (int i = 0; i < WM; ++i)
-#pragma unroll
-            for (int j = 0; j < WN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+      for (int i = 0; i < 4; ++i) {
+        c0a[i] = n0a[i];
+        c0b[i] = n0b[i];
+        sa[i] = nsa[i];
+        sbv[i] = nsb[i];
       }
     }
-  }
+  };
+  int64_t st = 0;
+  for (; st + NS < nst; ++st) stage(st, std::true_type{}, std::true_type{});
+  for (; st + 1 < nst; ++st) stage(st, std::true_type{}, std::false_type{});
+  stage(st, std::false_type{}, std::false_type{});
+  wait_vmcnt<0>();  // nothing is in flight here; the epilogue's barrier does not know of the asm DMA
   __syncthreads();  // every wave is done with the ring before the epilogue reuses the LDS
 
-  // ---- epilogues.  acc[i][j][q]: row = wm*32*WM + 32 i + 8 (q/4) + 4 g + q%4, col = r
+  // ---- epilogues.  acc[i][j][q]: tile row a_row0 + 32 i + 8 (q/4) + 4 g + q%4,
+  // tile column b_row0 + 32 j + r
   if (MODE == kGateUp) {
     float* hbuf = reinterpret_cast<float*>(smem);
     const float alpha_g = 1.0f / (a.a_gs[0] * a.b_gs[2 * e]);
     const float alpha_u = 1.0f / (a.a_gs[0] * a.b_gs[2 * e + 1]);
 #pragma unroll
-    for (int i = 0; i < WM; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < WN / 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int row = wm * 32 * WM + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3);
-          const int hc = wn * 16 * WN + 32 * j + r;
+          const int row = a_row0 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3);
+          const int hc = b_row0 / 2 + 32 * j + r;  // h column inside the tile
           const float gv = acc[i][j][q] * alpha_g;
-          const float uv = acc[i][j + WN / 2][q] * alpha_u;
+          const float uv = acc[i][j + 2][q] * alpha_u;
           hbuf[row * S::kHStride + hc] = silu(gv) * uv;
         }
     __syncthreads();
     const float gsh = a.h_gs[e];
     constexpr int kBlkPerRow = S::kHcols / 16;
-    for (int b = tid; b < BM * kBlkPerRow; b += 256) {
+    for (int b = tid; b < S::kARows * kBlkPerRow; b += 256) {
       const int row = b / kBlkPerRow, cb = b % kBlkPerRow;
       if (row >= rows_here) continue;
       float h[16];
@@ -616,32 +559,33 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
       uint32_t lo, hi;
       const uint32_t sc = quantize_block16(h, gsh, lo, hi);
       const int64_t hrow = off + row0 + row;
-      const int64_t hcol = (int64_t)nt * S::kHcols + 16 * cb;
+      // h columns 0..127 of the tile belong to n-tile nt, 128..255 (WIDE) to nt2
+      const int64_t hcol = (int64_t)(cb < 8 ? nt : nt2) * Tiled::kHcols + 16 * (cb % 8);
       *reinterpret_cast<uint2*>(a.h_codes + hrow * (a.I / 2) + hcol / 2) = make_uint2(lo, hi);
       a.h_scales[hrow * (a.I / 16) + hcol / 16] = (uint8_t)sc;
     }
   } else {
-    float* sqbuf = reinterpret_cast<float*>(smem + (S::kLds - 2 * BM * 4));
+    // Σf² partials [n-tile half][wn][128 rows] (full tiles: [wn][256 rows])
+    float* sqbuf = reinterpret_cast<float*>(smem + (Tiled::kLds - Tiled::kSqBytes));
     // the tile's pair ids and weights, staged once in the (now free) ring
     int32_t* prow = reinterpret_cast<int32_t*>(smem);
-    float* wrow = reinterpret_cast<float*>(smem + BM * 4);
-    for (int t = tid; t < BM; t += 256) {
+    float* wrow = reinterpret_cast<float*>(smem + S::kARows * 4);
+    for (int t = tid; t < S::kARows; t += 256) {
       const int32_t p = t < rows_here ? a.sorted[off + row0 + t] : 0;
       prow[t] = p;
       wrow[t] = t < rows_here ? a.topk_w[p] : 0.0f;
     }
     __syncthreads();
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
-    // v[16 i + q]: this lane's sum of f^2 over its WN columns of row (i, q)
-    constexpr int NV = WM * 16;
-    static_assert(NV % 32 == 0, "row partials must split evenly over 32 lanes");
-    float v[NV];
+    const int64_t col0 = (int64_t)((WIDE && wm) ? nt2 : nt) * Tiled::BN + 128 * wn;  // this wave's first column
+    // v[16 i + q]: this lane's sum of f^2 over its 4 columns of row (i, q)
+    float v[64];
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int qh = 0; qh < 4; ++qh) {
         // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
-        const int rb = wm * 32 * WM + 32 * i + 8 * qh + 4 * g;
+        const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
         const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
         const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
 #pragma unroll
@@ -652,10 +596,10 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
           const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
           float ss = 0.0f;
 #pragma unroll
-          for (int j = 0; j < WN; ++j) {
+          for (int j = 0; j < 4; ++j) {
             const float f = acc[i][j][q] * alpha;
             ss += f * f;
-            if (ok) a.pair_out[p * a.H + (int64_t)nt * BN + wn * 32 * WN + 32 * j + r] = wp * f;
+            if (ok) a.pair_out[p * a.H + col0 + 32 * j + r] = wp * f;
           }
           v[16 * i + q] = ss;
         }
@@ -665,10 +609,10 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
     // transposed butterfly: at each level a lane keeps half of its remaining
     // rows and sends the other half to its partner (lane ^ mask), so the
     // shuffles of a level are independent.  Afterwards lane r holds the sums of
-    // rows 16 i + q = (NV / 32) r + k.  The order is fixed: deterministic.
+    // rows 16 i + q = 2 r + k.  The order is fixed: deterministic.
 #pragma unroll
     for (int lvl = 0; lvl < 5; ++lvl) {
-      const int mask = 16 >> lvl, half = (NV >> lvl) / 2;
+      const int mask = 16 >> lvl, half = 32 >> lvl;
       const bool up = (r & mask) != 0;
 #pragma unroll
       for (int k = 0; k < half; ++k) {
@@ -677,14 +621,43 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
         v[k] = keep + __shfl_xor(send, mask, 32);
       }
     }
+    // full tiles: sqbuf[wn][row]; wide tiles: sqbuf[wm][wn][row], wm = the n-tile
+    float* sqw = sqbuf + (WIDE ? wm * 256 + wn * 128 : wn * 256);
 #pragma unroll
-    for (int k = 0; k < NV / 32; ++k) {
-      const int idx = (NV / 32) * r + k, i = idx >> 4, q = idx & 15;
-      sqbuf[wn * BM + wm * 32 * WM + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[k];
+    for (int k = 0; k < 2; ++k) {
+      const int idx = 2 * r + k, i = idx >> 4, q = idx & 15;
+      sqw[a_row0 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[k];
     }
     __syncthreads();
-    if (a.sq_part != nullptr && tid < BM && tid < rows_here)
-      a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = sqbuf[tid] + sqbuf[BM + tid];
+    if (a.sq_part != nullptr) {
+      if (WIDE) {
+        const int h = tid >> 7, row = tid & 127;  // 256 threads: 2 n-tiles x 128 rows
+        if (row < rows_here)
+          a.sq_part[(int64_t)prow[row] * a.n_part + (h ? nt2 : nt)] = sqbuf[h * 256 + row] + sqbuf[h * 256 + 128 + row];
+      } else if (tid < rows_here) {
+        a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = sqbuf[tid] + sqbuf[256 + tid];
+      }
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
+  const int nt = blockIdx.x;
+  const int mt = blockIdx.y;
+  if (mt >= a.num_tiles[0]) return;
+  const int e = a.tile_expert[mt];
+  const int row0 = a.tile_row0[mt];
+  const int off = a.offsets[e];
+  const int rows_here = min(Tiled::BM, a.offsets[e + 1] - off - row0);
+  // a half-empty m-tile runs wide over n-tiles nt and nt + gx / 2 (gx = gridDim.x even)
+  const int half = (int)(gridDim.x >> 1);
+  const bool wide = rows_here <= 128 && (gridDim.x & 1) == 0;
+  if (wide) {
+    if (nt >= half) return;
+    tiled_tile<MODE, true>(a, nt, nt + half, e, row0, off, rows_here);
+  } else {
+    tiled_tile<MODE, false>(a, nt, nt, e, row0, off, rows_here);
   }
 }
 
@@ -732,18 +705,6 @@ __global__ void sq_reduce_kernel(const float* __restrict__ part, int64_t npairs,
 // ---------------------------------------------------------------------------
 // host side
 
-#ifndef MOE_TILED_WM
-#define MOE_TILED_WM 4
-#endif
-#ifndef MOE_TILED_WN
-#define MOE_TILED_WN 4
-#endif
-#ifndef MOE_TILED_NS
-#define MOE_TILED_NS 4
-#endif
-constexpr int kTiledWM = MOE_TILED_WM, kTiledWN = MOE_TILED_WN, kTiledNS = MOE_TILED_NS;
-using Tiled = TiledShape<kTiledWM, kTiledWN, kTiledNS>;
-
 int64_t ffn_max_tiles(int64_t T, int64_t k, int64_t E) { return (T * k + Tiled::BM - 1) / Tiled::BM + E; }
 int ffn_sq_parts(int64_t H) { return (int)(H / 64); }  // small kernel: 64-column tiles (the finest split)
 bool ffn_use_small(int64_t T) { return T <= kSmallRows; }
@@ -769,20 +730,16 @@ hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool buil
   }
   const unsigned gy = (unsigned)ffn_max_tiles(T, a.k, E);
   // the tiles need more than the default 64 KiB of dynamic LDS
-  if (hipError_t e = set_max_dynamic_lds(
-          reinterpret_cast<const void*>(&ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>), Tiled::kLds))
+  if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ffn_tiled_kernel<kGateUp>), Tiled::kLds))
     return e;
-  if (hipError_t e = set_max_dynamic_lds(
-          reinterpret_cast<const void*>(&ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>), Tiled::kLds))
+  if (hipError_t e = set_max_dynamic_lds(reinterpret_cast<const void*>(&ffn_tiled_kernel<kDown>), Tiled::kLds))
     return e;
   if (mode == kGateUp) {
     const unsigned gx = (unsigned)(a.I / Tiled::kHcols);
-    hipLaunchKernelGGL((ffn_tiled_kernel<kGateUp, kTiledWM, kTiledWN, kTiledNS>), dim3(gx, gy), dim3(256), Tiled::kLds,
-                       st, a);
+    hipLaunchKernelGGL(ffn_tiled_kernel<kGateUp>, dim3(gx, gy), dim3(256), Tiled::kLds, st, a);
   } else {
     const unsigned gx = (unsigned)(a.H / Tiled::BN);
-    hipLaunchKernelGGL((ffn_tiled_kernel<kDown, kTiledWM, kTiledWN, kTiledNS>), dim3(gx, gy), dim3(256), Tiled::kLds, st,
-                       a);
+    hipLaunchKernelGGL(ffn_tiled_kernel<kDown>, dim3(gx, gy), dim3(256), Tiled::kLds, st, a);
   }
   return hipGetLastError();
 }

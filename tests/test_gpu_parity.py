@@ -277,6 +277,11 @@ def test_layer_parity_config0(ops):
     ("many_empty_experts", 40, 256, 128, 256, 8),
     ("tiled_mid", 130, 768, 384, 6, 3),
     ("tiled_k5", 40, 512, 640, 4, 2),  # down K = 640: five ring stages (one past the ring depth)
+    # one expert, k = 1: its m-tiles hold exactly T rows.  A last m-tile of <= 128 rows runs wide
+    # (128 rows x two n-tiles) when the n-tile count is even (here 2 for both stages)
+    ("e1_rows128_wide", 128, 512, 256, 1, 1),
+    ("e1_rows129_full", 129, 512, 256, 1, 1),
+    ("e1_rows384_full_then_wide", 384, 512, 256, 1, 1),
     ("stream_decode", 12, 2048, 2048, 8, 2),  # persistent decode kernel: K >= 2048, K % 1024 == 0
     ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: three K steps per wave and item
 ])
