@@ -48,14 +48,23 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 round-to-nearest-even of a float, saturating at 6; sign from the sign
-// bit of v.  Each comparison is one decision boundary of the value set; at
-// the boundary itself the tie goes to the even code: 0.25 -> 0, 0.75 -> 1.0,
-// 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0.
-__device__ __forceinline__ uint32_t e2m1_encode(float v) {
-  float a = __builtin_fabsf(v);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
+// Eight E2M1 codes of v[0..7] in one dword (element 2j in the low nibble of
+// byte j): round to nearest even on the value set {0, 0.5, 1, 1.5, 2, 3, 4,
+// 6}, saturating at 6, sign from the sign bit of v (so a small negative value
+// gives -0).  At a boundary the tie goes to the even code: 0.25 -> 0,
+// 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0.
+// As comparisons on a = |v|, the code magnitude is (a > 0.25) + (a >= 0.75) +
+// (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5).  The hardware
+// convert with scale 1.0 implements exactly this rule: it was compared with
+// that expression on the device, in both operand slots, for every non-NaN
+// float32.  The byte selector must be a literal, hence the four calls.
+__device__ __forceinline__ uint32_t e2m1_encode8(const float* v) {
+  uint32_t d = 0u;
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[0], v[1], 1.0f, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[2], v[3], 1.0f, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[4], v[5], 1.0f, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[6], v[7], 1.0f, 3);
+  return d;
 }
 
 // Quantize one block of 16 floats against global scale gs.  Returns the E4M3
@@ -74,10 +83,11 @@ __device__ __forceinline__ uint32_t quantize_block16(const float* x, float gs, u
   hi = 0;
   if (sd != 0.0f) {
     float inv = gs / sd;
+    float v[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= e2m1_encode(x[i] * inv) << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= e2m1_encode(x[8 + i] * inv) << (4 * i);
+    for (int i = 0; i < 16; ++i) v[i] = x[i] * inv;
+    lo = e2m1_encode8(v);
+    hi = e2m1_encode8(v + 8);
   }
   return sc;
 }
