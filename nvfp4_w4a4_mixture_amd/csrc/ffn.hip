@@ -550,6 +550,9 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     __syncthreads();
     const float gsh = a.h_gs[e];
     constexpr int kBlkPerRow = S::kHcols / 16;
+    // 8 independent blocks per thread, unrolled so that one block's LDS reads
+    // overlap another's arithmetic (one wave per SIMD)
+#pragma unroll 4
     for (int b = tid; b < S::kARows * kBlkPerRow; b += 256) {
       const int row = b / kBlkPerRow, cb = b % kBlkPerRow;
       if (row >= rows_here) continue;
