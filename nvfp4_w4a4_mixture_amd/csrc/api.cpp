@@ -62,19 +62,15 @@ moe_status launched(hipError_t e, const char* what) {
 
 // ---- FFN workspace layout
 struct FfnWs {
-  size_t tile_expert, tile_row0, num_tiles, sq_part, h_codes, h_scales, total_stage, total_full;
+  size_t tile_info, sq_part, h_codes, h_scales, total_stage, total_full;
 };
 
 FfnWs ffn_ws_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
   FfnWs w{};
   const int64_t tiles = moe::ffn_max_tiles(T, k, E);
   size_t o = 0;
-  w.tile_expert = o;
-  o = round_up(o + (size_t)tiles * 4, 256);
-  w.tile_row0 = o;
-  o = round_up(o + (size_t)tiles * 4, 256);
-  w.num_tiles = o;
-  o = round_up(o + 4, 256);
+  w.tile_info = o;
+  o = round_up(o + (size_t)tiles * 16, 256);
   w.sq_part = o;
   o = round_up(o + (size_t)(T * k) * (size_t)moe::ffn_sq_parts(H) * 4, 256);
   w.total_stage = o;
@@ -224,9 +220,7 @@ static moe_status gate_up_impl(const uint8_t* x_codes, const uint8_t* x_scales, 
   a.k = (int)k;
   a.offsets = expert_offsets;
   a.sorted = sorted_pair_ids;
-  a.tile_expert = reinterpret_cast<const int32_t*>(ws + L.tile_expert);
-  a.tile_row0 = reinterpret_cast<const int32_t*>(ws + L.tile_row0);
-  a.num_tiles = reinterpret_cast<const int32_t*>(ws + L.num_tiles);
+  a.tile_info = reinterpret_cast<const int32_t*>(ws + L.tile_info);
   a.h_codes = h_codes;
   a.h_scales = h_scales;
   return launched(moe::launch_ffn_stage(0, a, T, E, /*build_schedule=*/true, st), "moe_nvfp4_gate_up_swiglu");
@@ -252,9 +246,7 @@ static moe_status down_impl(const uint8_t* h_codes, const uint8_t* h_scales, con
   a.offsets = expert_offsets;
   a.sorted = sorted_pair_ids;
   a.topk_w = topk_w;
-  a.tile_expert = reinterpret_cast<const int32_t*>(ws + L.tile_expert);
-  a.tile_row0 = reinterpret_cast<const int32_t*>(ws + L.tile_row0);
-  a.num_tiles = reinterpret_cast<const int32_t*>(ws + L.num_tiles);
+  a.tile_info = reinterpret_cast<const int32_t*>(ws + L.tile_info);
   a.pair_out = pair_out;
   a.sq_part = pair_sqnorm ? reinterpret_cast<float*>(ws + L.sq_part) : nullptr;
   a.n_part = moe::ffn_use_small(T) ? (int)(H / 64) : (int)(H / moe::ffn_tiled_bn());

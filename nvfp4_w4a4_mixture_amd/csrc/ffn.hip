@@ -648,11 +648,11 @@ template <int MODE>
 __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
   const int nt = blockIdx.x;
   const int mt = blockIdx.y;
-  if (mt >= a.num_tiles[0]) return;
-  const int e = a.tile_expert[mt];
-  const int row0 = a.tile_row0[mt];
-  const int off = a.offsets[e];
-  const int rows_here = min(Tiled::BM, a.offsets[e + 1] - off - row0);
+  // one load for the tile's expert, first pair row and row count
+  const int4 ti = reinterpret_cast<const int4*>(a.tile_info)[mt];
+  const int rows_here = ti.z;
+  if (rows_here <= 0) return;  // past the last m-tile
+  const int e = ti.x, row0 = 0, off = ti.y;
   // a half-empty m-tile runs wide over n-tiles nt and nt + gx / 2 (gx = gridDim.x even)
   const int half = (int)(gridDim.x >> 1);
   const bool wide = rows_here <= 128 && (gridDim.x & 1) == 0;
@@ -668,10 +668,11 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 // schedule + final reduction kernels
 
 // m-tiles of every expert, in expert order: tile i -> (expert, first row).
+// m-tile schedule from the device-side expert offsets: slot i of the first
+// sum_e ceil(n_e / BM) holds {expert, first pair row, rows (<= BM), 0} in
+// expert order, the remaining slots up to n_slots hold rows 0.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int BM,
-                                                          int32_t* __restrict__ tile_expert,
-                                                          int32_t* __restrict__ tile_row0,
-                                                          int32_t* __restrict__ num_tiles) {
+                                                          int n_slots, int32_t* __restrict__ tile_info) {
   __shared__ int32_t base[257];
   const int e = threadIdx.x;
   const int cnt = (e < E) ? (offsets[e + 1] - offsets[e]) : 0;
@@ -686,14 +687,15 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
       run += v;
     }
     base[E] = run;
-    num_tiles[0] = run;
   }
   __syncthreads();
+  int4* info = reinterpret_cast<int4*>(tile_info);
   if (e < E)
     for (int i = 0; i < nt; ++i) {
-      tile_expert[base[e] + i] = e;
-      tile_row0[base[e] + i] = i * BM;
+      const int rows = cnt - i * BM < BM ? cnt - i * BM : BM;
+      info[base[e] + i] = make_int4(e, offsets[e] + i * BM, rows, 0);
     }
+  for (int i = base[E] + e; i < n_slots; i += 256) info[i] = make_int4(0, 0, 0, 0);
 }
 
 __global__ void sq_reduce_kernel(const float* __restrict__ part, int64_t npairs, int n_part, float* __restrict__ out) {
@@ -728,8 +730,7 @@ hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool buil
   if (build_schedule) {
     // m-tile schedule from the device-side expert offsets (no host readback)
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, st, a.offsets, (int)E, Tiled::BM,
-                       const_cast<int32_t*>(a.tile_expert), const_cast<int32_t*>(a.tile_row0),
-                       const_cast<int32_t*>(a.num_tiles));
+                       (int)ffn_max_tiles(T, a.k, E), const_cast<int32_t*>(a.tile_info));
   }
   const unsigned gy = (unsigned)ffn_max_tiles(T, a.k, E);
   // the tiles need more than the default 64 KiB of dynamic LDS

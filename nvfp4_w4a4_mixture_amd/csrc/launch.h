@@ -44,9 +44,9 @@ struct FfnArgs {
   const int32_t* offsets;
   const int32_t* sorted;
   const float* topk_w;
-  const int32_t* tile_expert;  // tiled schedule (workspace)
-  const int32_t* tile_row0;
-  const int32_t* num_tiles;
+  // tiled schedule (workspace): per m-tile slot {expert, first pair row, rows, 0};
+  // rows 0 marks a slot past the last m-tile
+  const int32_t* tile_info;
   uint8_t* h_codes;  // gate_up output
   uint8_t* h_scales;
   float* pair_out;  // down outputs
