@@ -611,24 +611,38 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     // Sum each row's partials over the 32 lanes of the half-wave with a
     // transposed butterfly: at each level a lane keeps half of its remaining
     // rows and sends the other half to its partner (lane ^ mask), so the
-    // shuffles of a level are independent.  Afterwards lane r holds the sums of
-    // rows 16 i + q = 2 r + k.  The order is fixed: deterministic.
+    // shuffles of a level are independent.  The masks go 1, 2, 8 (in-register
+    // DPP moves: 56 of the 62 shuffles) and then 4, 16 (LDS swizzles).  Lane r
+    // then holds the sums of rows 16 i + q = k + 32 r0 + 16 r1 + 8 r3 + 4 r2 +
+    // 2 r4 (r_b: bit b of r), k = 0, 1.  The order is fixed: deterministic.
+    auto xshfl = [](float x, int mask) -> float {
+      const int xi = __float_as_int(x);
+      int y;
+      if (mask == 1) y = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
+      else if (mask == 2) y = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+      else if (mask == 8) y = __builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false);  // row_ror:8 (16-lane rows)
+      else if (mask == 4) y = __builtin_amdgcn_ds_swizzle(xi, 0x101F);               // xor 4 within 32 lanes
+      else y = __builtin_amdgcn_ds_swizzle(xi, 0x401F);                              // xor 16 within 32 lanes
+      return __int_as_float(y);
+    };
+    constexpr int kMask[5] = {1, 2, 8, 4, 16};
 #pragma unroll
     for (int lvl = 0; lvl < 5; ++lvl) {
-      const int mask = 16 >> lvl, half = 32 >> lvl;
+      const int mask = kMask[lvl], half = 32 >> lvl;
       const bool up = (r & mask) != 0;
 #pragma unroll
       for (int k = 0; k < half; ++k) {
         const float send = up ? v[k] : v[k + half];
         const float keep = up ? v[k + half] : v[k];
-        v[k] = keep + __shfl_xor(send, mask, 32);
+        v[k] = keep + xshfl(send, mask);
       }
     }
     // full tiles: sqbuf[wn][row]; wide tiles: sqbuf[wm][wn][row], wm = the n-tile
     float* sqw = sqbuf + (WIDE ? wm * 256 + wn * 128 : wn * 256);
+    const int rbase = 32 * (r & 1) + 16 * ((r >> 1) & 1) + 8 * ((r >> 3) & 1) + 4 * ((r >> 2) & 1) + 2 * (r >> 4);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int idx = 2 * r + k, i = idx >> 4, q = idx & 15;
+      const int idx = rbase + k, i = idx >> 4, q = idx & 15;
       sqw[a_row0 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[k];
     }
     __syncthreads();
