@@ -30,7 +30,11 @@ __device__ __forceinline__ void combine_one(const float* __restrict__ pair_out, 
     float4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (u < n) v[u] = src[(int64_t)(j0 + u) * h4];
+      if (u < n) {
+        // each pair row is read once: non-temporal
+        const float4_t t = __builtin_nontemporal_load(reinterpret_cast<const float4_t*>(src + (int64_t)(j0 + u) * h4));
+        v[u] = make_float4(t[0], t[1], t[2], t[3]);
+      }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < n) {
