@@ -602,7 +602,9 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
           for (int j = 0; j < 4; ++j) {
             const float f = acc[i][j][q] * alpha;
             ss += f * f;
-            if (ok) a.pair_out[p * a.H + col0 + 32 * j + r] = wp * f;
+            // written once and read once by the combine: non-temporal, so the
+            // weighted rows do not push the operand tiles out of L2
+            if (ok) __builtin_nontemporal_store(wp * f, &a.pair_out[p * a.H + col0 + 32 * j + r]);
           }
           v[16 * i + q] = ss;
         }
