@@ -30,7 +30,9 @@
 //    32x32x16 MFMA, 2x2 waves of 128x128 each (16 accumulator tiles per wave:
 //    8 decoded fragments feed 16 MFMAs per k-step).  One barrier per stage,
 //    mid-stage; the fragment reads of the next half-stage and the FP4 decode
-//    of the next k-step run beside the current k-step's MFMAs.
+//    of the next k-step run beside the current k-step's MFMAs.  An expert's
+//    last m-tile with at most 128 pair rows runs wide instead: 128 rows
+//    against two n-tiles, 1x4 waves, a 3-stage ring.
 #include <type_traits>
 
 #include "device_common.h"
@@ -277,8 +279,8 @@ static_assert(TileShape<false>::kHcols == Tiled::kHcols && TileShape<false>::kBR
                   TileShape<false>::kARows == Tiled::BM, "full tile shape");
 static_assert(Tiled::kLds <= 160 * 1024, "LDS");
 
-// One tile: rows row0 .. row0 + rows_here - 1 of expert e's pairs against
-// n-tile nt (and nt2 when WIDE).
+// One tile: expert e's pair rows off + row0 .. off + row0 + rows_here - 1
+// (rows of the expert-sorted pair order) against n-tile nt (and nt2 when WIDE).
 template <int MODE, bool WIDE>
 __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, int e, int row0, int off,
                                            int rows_here) {
@@ -683,7 +685,6 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
 // ---------------------------------------------------------------------------
 // schedule + final reduction kernels
 
-// m-tiles of every expert, in expert order: tile i -> (expert, first row).
 // m-tile schedule from the device-side expert offsets: slot i of the first
 // sum_e ceil(n_e / BM) holds {expert, first pair row, rows (<= BM), 0} in
 // expert order, the remaining slots up to n_slots hold rows 0.
