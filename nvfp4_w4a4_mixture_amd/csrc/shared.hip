@@ -19,6 +19,8 @@
 //    128 x 64, operand tiles streamed into a 4-stage LDS ring by DMA.  Stage
 //    1's tile pairs 32 gate rows with the 32 up rows of the same h columns in
 //    each wave, so SwiGLU is applied in registers.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -179,16 +181,6 @@ __global__ __launch_bounds__(512) void dense_ring_kernel(const uint16_t* __restr
     a_off[i] = (uint32_t)(t * lda * 2) + 16 * chunk;
     b_off[i] = (uint32_t)(b_row(row) * K * 2) + 16 * chunk;
   }
-  auto issue = [&](int64_t st) {
-    unsigned char* base = smem + (int)(st % NS) * kStage;
-    const unsigned char* ag = reinterpret_cast<const unsigned char*>(a) + st * 64;
-    const unsigned char* bg = reinterpret_cast<const unsigned char*>(w) + st * 64;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(ag + a_off[i], base + (8 * i + wave) * 1024);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(bg + b_off[i], base + kTile + (8 * i + wave) * 1024);
-  };
-
   float16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -204,51 +196,82 @@ __global__ __launch_bounds__(512) void dense_ring_kernel(const uint16_t* __restr
   const uint32_t slot0 = 16u * (uint32_t)((2 * 0 + g) ^ ((r >> 2) & 3));
   const uint32_t slot1 = 16u * (uint32_t)((2 * 1 + g) ^ ((r >> 2) & 3));
 
-  const int64_t nst = K / 32;
+  // Pipelined ring, as in the FFN tile kernel: the DMA is inline asm (so the
+  // compiler's own LDS reads get no blanket vmcnt(0)), one barrier per stage
+  // between its two k-steps, and each k-step's fragments are read while the
+  // previous k-step's MFMAs run.  The prologue fills all NS slots; at the
+  // mid-stage barrier of stage st every wave has read slot st % NS
+  // (lgkmcnt(0) before the barrier) and waited for stage st + 1, so stage
+  // st + NS is issued into slot st % NS right after it.
+  const int64_t nst = K / 32;  // >= 4 (K % 128 == 0)
+  constexpr int L = kLoadsPerStage;
+  const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
+  auto issue = [&](int64_t st) {
+    const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(st % NS) * (uint32_t)kStage);
+    const unsigned char* ag = reinterpret_cast<const unsigned char*>(a) + st * 64;
+    const unsigned char* bg = reinterpret_cast<const unsigned char*>(w) + st * 64;
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nst) issue(p);
-  for (int64_t st = 0; st < nst; ++st) {
-    const int64_t ahead = nst - 1 - st;
-    if (ahead >= NS - 2) wait_vmcnt<kLoadsPerStage * (NS - 2)>();
-    else if (ahead == 1) wait_vmcnt<kLoadsPerStage>();
-    else wait_vmcnt<0>();
-    // bare s_barrier: every wave's DMA for stage st has landed and stage st-1's buffer is read
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const uint32_t sb = lds_base + (uint32_t)(st % NS) * kStage;
-    const uint32_t a0 = sb + a_lane + slot0, a1 = sb + a_lane + slot1;
-    const uint32_t b0 = sb + b_lane + slot0, b1 = sb + b_lane + slot1;
-    u32x4_t fa[2][4], fb[2][2];
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n"
-        "ds_read_b128 %1, %12 offset:2048\n"
-        "ds_read_b128 %2, %12 offset:4096\n"
-        "ds_read_b128 %3, %12 offset:6144\n"
-        "ds_read_b128 %4, %13 offset:0\n"
-        "ds_read_b128 %5, %13 offset:2048\n"
-        "ds_read_b128 %6, %14 offset:0\n"
-        "ds_read_b128 %7, %14 offset:2048\n"
-        "ds_read_b128 %8, %14 offset:4096\n"
-        "ds_read_b128 %9, %14 offset:6144\n"
-        "ds_read_b128 %10, %15 offset:0\n"
-        "ds_read_b128 %11, %15 offset:2048\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=&v"(fa[0][0]), "=&v"(fa[0][1]), "=&v"(fa[0][2]), "=&v"(fa[0][3]), "=&v"(fb[0][0]), "=&v"(fb[0][1]),
-          "=&v"(fa[1][0]), "=&v"(fa[1][1]), "=&v"(fa[1][2]), "=&v"(fa[1][3]), "=&v"(fb[1][0]), "=&v"(fb[1][1])
-        : "v"(a0), "v"(b0), "v"(a1), "v"(b1)
-        : "memory");
+    for (int i = 0; i < 2; ++i) dma16_async(ag, a_off[i], sb + (8 * i + wave_u) * 1024u);
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int i = 0; i < 2; ++i) dma16_async(bg, b_off[i], sb + (uint32_t)kTile + (8 * i + wave_u) * 1024u);
+  };
+  auto load_k = [&](int64_t st, uint32_t slot, u32x4_t* fa, u32x4_t* fb) {
+    const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)kStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const u32x4_t*>(smem + sb + a_lane + slot + 2048u * i);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[s2][i]), as_bf16x8(fb[s2][j]), acc[i][j],
-                                                              0, 0, 0);
-  }
+    for (int j = 0; j < 2; ++j) fb[j] = *reinterpret_cast<const u32x4_t*>(smem + sb + b_lane + slot + 2048u * j);
+  };
+  auto mfma8 = [&](const u32x4_t* fa, const u32x4_t* fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j], 0, 0, 0);
+    // each MFMA followed by one of the 6 LDS reads issued before it in program order
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (m < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < NS; ++p) issue(p);
+  wait_vmcnt<3 * L>();  // stage 0 has landed (nst >= NS)
+  barrier_after_lds();
+  u32x4_t f0a[4], f0b[2];
+  load_k(0, slot0, f0a, f0b);
+  auto stage = [&](int64_t st, auto more_c, auto issue_c) {
+    constexpr bool kMore = decltype(more_c)::value, kIssue = decltype(issue_c)::value;
+    u32x4_t f1a[4], f1b[2], n0a[4], n0b[2];
+    __builtin_amdgcn_sched_barrier(0);
+    load_k(st, slot1, f1a, f1b);
+    mfma8(f0a, f0b);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kMore) {
+      // stage st + 1 has landed; the stages issued after it may stay in flight
+      const int64_t ahead = nst - 2 - st;
+      if (kIssue || ahead >= NS - 2) wait_vmcnt<(NS - 2) * L>();
+      else if (ahead == 1) wait_vmcnt<L>();
+      else wait_vmcnt<0>();
+      barrier_after_lds();
+      if constexpr (kIssue) issue(st + NS);
+      load_k(st + 1, slot0, n0a, n0b);
+    }
+    mfma8(f1a, f1b);
+    if constexpr (kMore) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f0a[i] = n0a[i];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) f0b[j] = n0b[j];
+    }
+  };
+  int64_t st = 0;
+  for (; st + NS < nst; ++st) stage(st, std::true_type{}, std::true_type{});
+  for (; st + 1 < nst; ++st) stage(st, std::true_type{}, std::false_type{});
+  stage(st, std::false_type{}, std::false_type{});
+  wait_vmcnt<0>();  // nothing is in flight here
 
   // ---- epilogues.  acc[i][j][e]: row wm*128 + 32 i + 8 (e/4) + 4 g + e%4, column r of B fragment j
   if (MODE == kSharedGateUp) {
