@@ -164,12 +164,27 @@ void ffn_small_kernel(FfnArgs a) {
   // flight while the current one is decoded and multiplied
   const int nit = (int)(K / KB);
   if (wave < nit) {
-    It cur, nxt;
-    load(wave, cur);
-    for (int it = wave; it < nit; it += 4) {
-      if (it + 4 < nit) load(it + 4, nxt);
-      compute(cur);
-      cur = nxt;
+    // Two buffers in turn, no copy between them (a copy of registers a load
+    // is still writing waits for that load), and the last iteration on a path
+    // of its own: every compute that has a prefetch in flight behind it waits
+    // only for its own loads.
+    It b0, b1;
+    load(wave, b0);
+    for (int it = wave;;) {
+      if (it + 4 >= nit) {
+        compute(b0);
+        break;
+      }
+      load(it + 4, b1);
+      compute(b0);
+      it += 4;
+      if (it + 4 >= nit) {
+        compute(b1);
+        break;
+      }
+      load(it + 4, b0);
+      compute(b1);
+      it += 4;
     }
   }
 
