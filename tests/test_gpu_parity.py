@@ -282,8 +282,10 @@ def test_layer_parity_config0(ops):
     ("e1_rows128_wide", 128, 512, 256, 1, 1),
     ("e1_rows129_full", 129, 512, 256, 1, 1),
     ("e1_rows384_full_then_wide", 384, 512, 256, 1, 1),
-    ("stream_decode", 12, 2048, 2048, 8, 2),  # persistent decode kernel: K >= 2048, K % 1024 == 0
-    ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: three K steps per wave and item
+    # decode kernel (T <= 16): four waves take 256-k iterations in turn through two register buffers
+    ("stream_decode", 12, 2048, 2048, 8, 2),  # 8 iterations: two per wave in both stages
+    ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: 12 iterations, three per wave (ends in the first buffer)
+    ("decode_uneven_waves", 10, 1280, 384, 8, 2),  # gate_up: 5 iterations (2, 1, 1, 1); down: K 384, 128-k steps
 ])
 def test_layer_parity_random(ops, name, T, H, I, E, k):
     case = random_case(name, zlib.crc32(name.encode()) % 1000, T, H, I, E, k)
