@@ -128,7 +128,7 @@ def _expert_getter(experts) -> ExpertSource:
 
 def moe_layer(x_bf16: np.ndarray, w_router_bf16: np.ndarray, bias: np.ndarray, k: int, rsf: float,
               gs_x, experts, gs_h: np.ndarray, tokens: Sequence[int] | None = None,
-              with_pairs: bool = False) -> dict:
+              with_pairs: bool = False, threads: int = 1) -> dict:
     """The routed MoE layer, end to end, on the CPU.
 
     ``experts`` is a sequence of :class:`ExpertQ` or a callable e -> ExpertQ
@@ -141,6 +141,9 @@ def moe_layer(x_bf16: np.ndarray, w_router_bf16: np.ndarray, bias: np.ndarray, k
     [len(tokens), H]) and, over the routed experts, ``saliency`` (float64 [E],
     only meaningful when ``tokens`` is None), ``pair_norm`` (||f_p||_2 per pair)
     and, if ``with_pairs``, ``pair_f`` (unweighted f per pair, [n*k, H]).
+    ``threads`` > 1 evaluates the experts concurrently; their contributions are
+    still added to y one expert after another in increasing expert order, so
+    the result does not depend on it.
     """
     get = _expert_getter(experts)
     x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
@@ -156,23 +159,41 @@ def moe_layer(x_bf16: np.ndarray, w_router_bf16: np.ndarray, bias: np.ndarray, k
     pair_f = np.zeros((n * k, H), dtype=np.float64) if with_pairs else None
     y = np.zeros((n, H), dtype=np.float64)
     flat = ids.reshape(-1)
-    for e in np.unique(flat):
+
+    def one(e):
         pairs = np.nonzero(flat == e)[0]
-        toks = pairs // k
         wg, wu, wd = get(int(e)).dequantized()
-        f, _ = expert_ffn(xhat[toks], wg, wu, wd, gs_h[e])
+        f, _ = expert_ffn(xhat[pairs // k], wg, wu, wd, gs_h[e])
+        return pairs, f
+
+    routed = [int(e) for e in np.unique(flat)]
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        ex = ThreadPoolExecutor(threads)
+        results = ex.map(one, routed)  # yields in expert order
+    else:
+        ex = None
+        results = map(one, routed)
+    for pairs, f in results:
+        toks = pairs // k
         pair_norm[pairs] = np.sqrt(np.sum(f * f, axis=1))
         if with_pairs:
             pair_f[pairs] = f
         # y_t += w_{t,j} f_p  (each pair appears once; order of j does not matter in fp64)
         np.add.at(y, toks, w64.reshape(-1)[pairs][:, None] * f)
+    if ex is not None:
+        ex.shutdown()
     sal = reap_saliency(pair_norm, w64, ids, E)
     return dict(ids=ids, weights=w32, weights64=w64, gap=gap, x_codes=xc, x_scales=xs, y=y,
                 saliency=sal, pair_norm=pair_norm, pair_f=pair_f)
 
 
 def expert_pairs_output(x_bf16_rows: np.ndarray, gs_x, expert: ExpertQ, gs_h_e) -> np.ndarray:
-    """Unweighted f for given token rows through one expert (for sampled checks)."""
+    """Unweighted f [M, H] of the given token rows through one expert, as the layer computes it.
+
+    Each row is quantized to NVFP4 with gs_x and dequantized (quantization is
+    per row, so the subset gives the same values as the whole batch), then
+    passed through :func:`expert_ffn` with the expert's calibrated gs_h."""
     xc, xs = nvfp4.quantize(bf16_to_f32(x_bf16_rows), gs_x)
     xhat = nvfp4.dequantize(xc, xs, gs_x)
     wg, wu, wd = expert.dequantized()

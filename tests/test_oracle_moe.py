@@ -215,3 +215,54 @@ def test_calibration_definition():
         assert gs_h[e] == np.float32(np.float32(2688.0) / np.max(np.abs(h)))
     # the calibration amax maps to the top code at the top scale
     assert moe.calibrate(xc, experts, E, threads=3)[1].tolist() == gs_h.tolist()
+
+
+def test_expert_pairs_output_equals_layer_pairs_and_loops():
+    """expert_pairs_output (the per-expert reference of the full-size checks) gives the
+    layer's own unweighted f for the same pairs, and a pure-Python loop on one expert:
+    a dropped NVFP4 quantization of x or of h, the wrong gs_h or a transposed weight
+    fails here."""
+    T, H, I, E, k = 7, 32, 16, 4, 2
+    x, wr, bias, experts, gs_x, gs_h = _rand_layer(31, T, H, I, E)
+    out = moe.moe_layer(x, wr, bias, k, 2.5, gs_x, experts, gs_h, with_pairs=True)
+    flat = out["ids"].reshape(-1)
+    checked = 0
+    for e in range(E):
+        pairs = np.nonzero(flat == e)[0]
+        if len(pairs) == 0:
+            continue
+        f = moe.expert_pairs_output(x[pairs // k], gs_x, experts[e], gs_h[e])
+        want = out["pair_f"][pairs]
+        assert np.max(np.abs(f - want)) <= 1e-13 * np.max(np.abs(want))
+        checked += 1
+    assert checked >= 2
+    # loops for expert 1 on three token rows, from the pinned quantizer and math.fsum
+    e, rows = 1, [0, 3, 6]
+    W = experts[e]
+    wg = nvfp4.dequantize_packed(W.gate_codes, W.gate_scales, W.gate_gs)
+    wu = nvfp4.dequantize_packed(W.up_codes, W.up_scales, W.up_gs)
+    wd = nvfp4.dequantize_packed(W.down_codes, W.down_scales, W.down_gs)
+    got = moe.expert_pairs_output(x[rows], gs_x, W, gs_h[e])
+    for n, t in enumerate(rows):
+        xf = gen.bf16_bits_to_f32(x[t:t + 1])
+        xc, xs = nvfp4.quantize(xf, gs_x)
+        xhat = nvfp4.dequantize(xc, xs, gs_x)[0]
+        h = []
+        for i in range(I):
+            g = math.fsum(xhat[c] * wg[i, c] for c in range(H))
+            u = math.fsum(xhat[c] * wu[i, c] for c in range(H))
+            h.append(float(np.float32(g / (1.0 + math.exp(-g)) * u)))
+        hc, hs = nvfp4.quantize(np.array([h], np.float32), gs_h[e])
+        hhat = nvfp4.dequantize(hc, hs, gs_h[e])[0]
+        for o in range(H):
+            f = math.fsum(hhat[i] * wd[o, i] for i in range(I))
+            assert abs(got[n, o] - f) <= 1e-12 * max(1.0, abs(f))
+
+
+def test_layer_threads_do_not_change_results():
+    T, H, I, E, k = 9, 32, 16, 5, 2
+    x, wr, bias, experts, gs_x, gs_h = _rand_layer(37, T, H, I, E)
+    a = moe.moe_layer(x, wr, bias, k, 2.5, gs_x, experts, gs_h, with_pairs=True)
+    b = moe.moe_layer(x, wr, bias, k, 2.5, gs_x, experts, gs_h, with_pairs=True, threads=4)
+    for key in ("ids", "y", "saliency", "pair_norm", "pair_f"):
+        assert np.array_equal(a[key], b[key]), key
