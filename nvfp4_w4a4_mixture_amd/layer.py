@@ -28,6 +28,8 @@ class LayerOut:
     pair_sqnorm: Optional[torch.Tensor]
     saliency: Optional[torch.Tensor]
     shared_out: Optional[torch.Tensor] = None  # the shared expert's FP32 output (block=True)
+    h_codes: Optional[torch.Tensor] = None  # re-quantized hidden state [T*k, I/2], rows in sorted-pair order
+    h_scales: Optional[torch.Tensor] = None  # its E4M3 block scales [T*k, I/16]
 
 
 class NVFP4MoELayer:
@@ -172,6 +174,6 @@ class NVFP4MoELayer:
             ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
         mark(4)
         return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal,
-                        b.get("shared_out"))
+                        b.get("shared_out"), b["h_codes"], b["h_scales"])
 
     __call__ = forward

@@ -129,16 +129,44 @@ def oracle_layer(case: Case, tokens=None, with_pairs=False) -> dict:
                           tokens=tokens, with_pairs=with_pairs)
 
 
-def check_routing(ids_gpu, w_gpu, ref: dict, rsf: float, E: int) -> int:
-    """Bitwise ids where the oracle's top-k margin is >= NEAR_TIE; returns the number of near-tie tokens.
+def check_routing(ids_gpu, w_gpu, ref: dict, rsf: float, E: int, x_bf16=None, wr_bf16=None, bias=None) -> int:
+    """Routing parity; returns the number of near-tie tokens.
 
-    For near-tie tokens the GPU choice must still be a valid top-k (its k-th
-    score within NEAR_TIE of the oracle's)."""
+    Tokens whose oracle top-k margin (score_(k) - score_(k+1)) is >= NEAR_TIE:
+    the GPU ids equal the oracle's bitwise and topk_w is within 1e-6 * rsf of
+    the oracle's FP64 weights.  Near-tie tokens (an exact tie included) may
+    legitimately pick another top-k when the two sides round a score
+    differently, so for them the GPU choice is checked for validity against
+    the oracle's FP64 scores, recomputed for those tokens from x, the router
+    and the bias: k distinct ids in [0, E); slots in descending score (each
+    within NEAR_TIE of the next); every chosen score >= every unchosen score -
+    NEAR_TIE; and topk_w = rsf * s_j / sum(s) over the GPU's own chosen set,
+    within 1e-6 * rsf."""
     ids_ref, gap = ref["ids"], ref["gap"]
+    ids_gpu = np.asarray(ids_gpu)
+    w_gpu = np.asarray(w_gpu)
+    k = ids_gpu.shape[1]
     clear = gap >= NEAR_TIE
     assert np.array_equal(ids_gpu[clear], ids_ref[clear]), "top-k ids differ"
     assert np.all(np.abs(w_gpu[clear].astype(np.float64) - ref["weights64"][clear]) <= 1e-6 * rsf), "topk_w differ"
-    return int((~clear).sum())
+    near = np.nonzero(~clear)[0]
+    if len(near) == 0:
+        return 0
+    if x_bf16 is None or wr_bf16 is None or bias is None:
+        raise AssertionError(f"{len(near)} near-tie tokens and no x/router/bias to validate them")
+    s = oroute.sigmoid(oroute.router_logits(np.asarray(x_bf16)[near], wr_bf16))
+    score = s + np.asarray(bias, np.float32).astype(np.float64)[None, :]
+    for n, t in enumerate(near):
+        sel = ids_gpu[t].astype(np.int64)
+        assert np.all((sel >= 0) & (sel < E)) and len(set(sel.tolist())) == k, f"token {t}: invalid ids {sel}"
+        sc = score[n, sel]
+        assert np.all(sc[:-1] >= sc[1:] - NEAR_TIE), f"token {t}: slots not in descending score"
+        rest = np.setdiff1d(np.arange(E), sel)
+        if len(rest):
+            assert sc.min() >= score[n, rest].max() - NEAR_TIE, f"token {t}: not a top-k"
+        w_want = rsf * s[n, sel] / np.sum(s[n, sel])
+        assert np.all(np.abs(w_gpu[t].astype(np.float64) - w_want) <= 1e-6 * rsf), f"token {t}: topk_w"
+    return int(len(near))
 
 
 def untile_weight_scales(s) -> np.ndarray:

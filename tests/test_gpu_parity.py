@@ -140,8 +140,7 @@ def test_route_and_permutation_bitexact(ops, T, H, E, k):
         return
     ids, w = to_np(out.topk_ids), to_np(out.topk_w)
     ref = dict(zip(("ids", "weights", "weights64", "gap"), oroute.route(xb, wr, bias, k, rsf)))
-    near = check_routing(ids, w, ref, rsf, E)
-    assert near == 0, f"{near} near-tie tokens"
+    check_routing(ids, w, ref, rsf, E, xb, wr, bias)
     c_ref, o_ref, p_ref = oracle_perm(ids, E)
     assert np.array_equal(counts, c_ref)
     assert np.array_equal(offsets, o_ref)
@@ -164,7 +163,7 @@ def test_route_strided_rows(ops, T, H, pad):
     xb = np.ascontiguousarray(xw[:, :H])
     ref = dict(zip(("ids", "weights", "weights64", "gap"), oroute.route(xb, wr, bias, k, rsf)))
     ids = to_np(out.topk_ids)
-    assert check_routing(ids, to_np(out.topk_w), ref, rsf, E) == 0
+    check_routing(ids, to_np(out.topk_w), ref, rsf, E, xb, wr, bias)
     c_ref, o_ref, p_ref = oracle_perm(ids, E)
     assert np.array_equal(to_np(out.expert_counts), c_ref)
     assert np.array_equal(to_np(out.expert_offsets), o_ref)
@@ -189,7 +188,7 @@ def test_route_quantize_matches_route_and_quantize(ops, T, H, E, k):
     assert np.array_equal(to_np(scales), s_ref)
     ids = to_np(out.topk_ids)
     ref = dict(zip(("ids", "weights", "weights64", "gap"), oroute.route(xb, wr, bias, k, 2.5)))
-    assert check_routing(ids, to_np(out.topk_w), ref, 2.5, E) == 0
+    check_routing(ids, to_np(out.topk_w), ref, 2.5, E, xb, wr, bias)
     c_ref, o_ref, p_ref = oracle_perm(ids, E)
     assert np.array_equal(to_np(out.expert_counts), c_ref)
     assert np.array_equal(to_np(out.expert_offsets), o_ref)
@@ -211,9 +210,47 @@ def test_route_exact_ties_go_to_lower_index(ops, T):
     xb = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     out = ops.moe_route(dev_bf16(xb), dev_bf16(wrb), torch.from_numpy(bias).cuda(), k, 1.0)
     ids = to_np(out.topk_ids)
-    ref_ids, _, _, _ = oroute.route(xb, wrb, bias, k, 1.0)
+    ref_ids, w32_ref, w64_ref, gap = oroute.route(xb, wrb, bias, k, 1.0)
     assert np.array_equal(ids, ref_ids)
+    # every token has an exact tie inside its top-k: validated as near-tie tokens too
+    check_routing(ids, to_np(out.topk_w), {"ids": ref_ids, "weights64": w64_ref, "gap": gap}, 1.0, E, xb, wrb, bias)
     assert np.all(ids[:, :3] == [2, 5, 9])
+
+
+@pytest.mark.parametrize("T,H,E,k,nan_bias", [(12, 256, 40, 6, False), (300, 512, 80, 8, True), (40, 64, 16, 16, False)])
+def test_route_nonfinite_inputs(ops, T, H, E, k, nan_bias):
+    """Tokens whose x holds a NaN or infinities (so their logits are NaN or infinite), and NaN
+    biases: the selection ranks NaN scores below every number, so ids and the permutation still
+    equal the oracle's (a stable descending sort, NaN last) and every slot is written."""
+    say(f"route nonfinite T={T} H={H} E={E} k={k} nan_bias={nan_bias}")
+    rng = np.random.default_rng(T + E)
+    xf = rng.standard_normal((T, H)).astype(np.float32)
+    xf[3, 7] = np.nan  # every logit of token 3 is NaN
+    xf[5, 11] = np.inf  # token 5: +-inf (or NaN where the router weight is 0)
+    xf[8, 2], xf[8, 9] = np.inf, -np.inf  # token 8: mixed
+    if T == 40:
+        xf[:] = np.nan  # every token NaN: ids 0..k-1 in order
+    xb = gen.f32_to_bf16_bits(np.where(np.isfinite(xf), xf, 0)).astype(np.uint16)
+    special = ~np.isfinite(xf)
+    xb[special] = np.where(np.isnan(xf[special]), 0x7FC0, np.where(xf[special] > 0, 0x7F80, 0xFF80)).astype(np.uint16)
+    wr = gen.f32_to_bf16_bits((rng.standard_normal((E, H)) * 0.05).astype(np.float32))
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    if nan_bias:
+        bias[[4, 17]] = np.nan
+    ids_ref, _, w64_ref, _ = oroute.route(xb, wr, bias, k, 2.5)
+    out = ops.moe_route(dev_bf16(xb), dev_bf16(wr), torch.from_numpy(bias).cuda(), k, 2.5)
+    torch.cuda.synchronize()
+    ids, w = to_np(out.topk_ids), to_np(out.topk_w).astype(np.float64)
+    assert np.array_equal(ids, ids_ref)
+    assert np.array_equal(np.isnan(w), np.isnan(w64_ref))
+    fin = ~np.isnan(w64_ref)
+    assert np.all(np.abs(w[fin] - w64_ref[fin]) <= 1e-6 * 2.5)
+    c_ref, o_ref, p_ref = oracle_perm(ids_ref, E)
+    assert np.array_equal(to_np(out.expert_counts), c_ref)
+    assert np.array_equal(to_np(out.expert_offsets), o_ref)
+    assert np.array_equal(to_np(out.sorted_pair_ids), p_ref)
+    if T == 40:
+        assert np.all(ids == np.arange(k))
 
 
 # ---------------------------------------------------------------------------
@@ -236,7 +273,7 @@ def _layer_check(ops, case, reap=True):
     torch.cuda.synchronize()
     ref = oracle_layer(case, with_pairs=True)
     ids, w = to_np(out32.route.topk_ids), to_np(out32.route.topk_w)
-    assert check_routing(ids, w, ref, case.rsf, case.E) == 0
+    check_routing(ids, w, ref, case.rsf, case.E, case.x, case.wr, case.bias)
     c_ref, s_ref = oracle_codes(case)
     assert np.array_equal(to_np(out32.x_codes), c_ref) and np.array_equal(to_np(out32.x_scales), s_ref)
     y32 = to_np(out32.y)

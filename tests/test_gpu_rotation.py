@@ -124,8 +124,8 @@ def test_rotated_outlier_layer_full_size(ops):
             wrr = orot.rotate_bf16(wr, signs, blk)
             from oracle import routing as oroute
             ids_ref, _, w64, gap = oroute.route(xr, wrr, bias, cfg.k, cfg.rsf)
-            assert check_routing(idss[blk][tok], to_np(out.route.topk_w)[tok],
-                                 {"ids": ids_ref, "weights64": w64, "gap": gap}, cfg.rsf, cfg.E) == 0
+            check_routing(idss[blk][tok], to_np(out.route.topk_w)[tok],
+                          {"ids": ids_ref, "weights64": w64, "gap": gap}, cfg.rsf, cfg.E, xr, wrr, bias)
             need = sorted(set(int(e) for e in ids_ref.reshape(-1)))
             q = {}
             for e, g, u, d in gen.iter_experts_bf16(ws, need):
