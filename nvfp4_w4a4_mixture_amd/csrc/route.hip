@@ -119,25 +119,41 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// z[i] = sum over splits s (in order) of pt[s * stride + ec[i]], i < NG.
+// Selection key of an FP64 score: a signed 64-bit integer in the order of the
+// scores, with -0 equal to +0 and NaN below every number (below -inf).  Keys
+// are totally ordered, so with ties going to the lower expert index every rank
+// 0..E-1 is taken by exactly one expert, also when scores are NaN (a token
+// whose x holds a NaN or an infinity, or a NaN bias).  This is the order of a
+// stable sort of the scores, descending, with NaN last.
+__device__ __forceinline__ long long score_key(double v) {
+  if (v != v) return (long long)0x8000000000000000ull;  // NaN: the smallest key
+  long long b = __double_as_longlong(v);
+  if (b == (long long)0x8000000000000000ull) b = 0;  // -0 -> +0
+  return b < 0 ? (b ^ 0x7FFFFFFFFFFFFFFFll) : b;      // negatives: larger magnitude, smaller key
+}
+
 // Top-k of one token by one wave from its scores.  Lane holds, for the
 // experts e = lane + 64 i (i < NG, e < E), sg = sigmoid(logit) and
 // sc = sg + bias.  The top-k are the experts whose rank under the total order
-// (score descending, expert ascending) is below k: each lane ranks its experts
-// against every score, broadcast from the wave's LDS row `row` (>= E + 1
-// doubles, 16-byte aligned; padded to an even length with -inf, which
-// outranks nothing), so slot j holds the j-th expert of that order.  The row
-// is then reused for the selected sg; weights are rsf * s_j / sum s, the sum
-// taken over j = 0..k-1 in order.  On return slot[i] = 1 + the slot of expert
-// lane + 64 i (0: not chosen).
+// (score key descending, expert ascending) is below k: each lane ranks its
+// experts against every key, broadcast from the wave's LDS row `row` (>= E + 1
+// doubles, 16-byte aligned; padded to an even length with the smallest key at
+// index E, which outranks nothing), so slot j holds the j-th expert of that
+// order.  The row is then reused for the selected sg; weights are
+// rsf * s_j / sum s, the sum taken over j = 0..k-1 in order.  On return
+// slot[i] = 1 + the slot of expert lane + 64 i (0: not chosen).
 template <int NG>
 __device__ __forceinline__ void rank_select(const double (&sg)[NG], const double (&sc)[NG], int64_t t, int E, int k,
                                             float rsf, int lane, double* row, int32_t* __restrict__ topk_ids,
                                             float* __restrict__ topk_w, int (&slot)[4]) {
+  long long* krow = reinterpret_cast<long long*>(row);
+  long long key[NG];
 #pragma unroll
-  for (int i = 0; i < NG; ++i)
-    if (lane + 64 * i < E) row[lane + 64 * i] = sc[i];
-  if (lane == 0 && (E & 1)) row[E] = -__builtin_inf();
+  for (int i = 0; i < NG; ++i) {
+    key[i] = score_key(sc[i]);
+    if (lane + 64 * i < E) krow[lane + 64 * i] = key[i];
+  }
+  if (lane == 0 && (E & 1)) krow[E] = (long long)0x8000000000000000ull;
   wave_lds_sync();
   int rank[NG];
 #pragma unroll
@@ -145,16 +161,16 @@ __device__ __forceinline__ void rank_select(const double (&sg)[NG], const double
   const int npair = (E + 1) >> 1;
 #pragma unroll 4
   for (int q = 0; q < npair; ++q) {
-    const double2 v = reinterpret_cast<const double2*>(row)[q];
+    const longlong2 v = reinterpret_cast<const longlong2*>(krow)[q];
     const int e0 = 2 * q;
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const int e = lane + 64 * i;
-      rank[i] += (int)(v.x > sc[i]) | ((int)(v.x == sc[i]) & (int)(e0 < e));
-      rank[i] += (int)(v.y > sc[i]) | ((int)(v.y == sc[i]) & (int)(e0 + 1 < e));
+      rank[i] += (int)(v.x > key[i]) | ((int)(v.x == key[i]) & (int)(e0 < e));
+      rank[i] += (int)(v.y > key[i]) | ((int)(v.y == key[i]) & (int)(e0 + 1 < e));
     }
   }
-  wave_lds_sync();  // every lane has read the scores; the row now takes sg by slot
+  wave_lds_sync();  // every lane has read the keys; the row now takes sg by slot
 #pragma unroll
   for (int i = 0; i < 4; ++i) slot[i] = 0;
 #pragma unroll
