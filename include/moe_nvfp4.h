@@ -94,7 +94,9 @@ int32_t moe_abi_version(void);
  *   logit[t,e] = sum_h x[t,h] * w_router[e,h]   (BF16 products, FP64 sums)
  *   s = sigmoid(logit) (FP64); score = s + bias[e]
  *   topk_ids[t, 0..k-1]: the k largest scores, descending; equal scores go to
- *     the lower expert index
+ *     the lower expert index, -0 equals +0, and a NaN score ranks below every
+ *     number (so a token whose x holds a NaN or an infinity, or a NaN bias,
+ *     still gets k distinct ids: those of a stable descending sort, NaN last)
  *   topk_w[t,j] = rsf * s_j / sum_{selected} s   (FP64, stored FP32; the
  *     bias selects, it does not enter the weights)
  *   expert_counts[e] = number of pairs routed to e
@@ -152,7 +154,10 @@ moe_status nvfp4_quantize_weights(const uint16_t* w_bf16, int64_t batch, int64_t
                                   void* stream);
 
 /* One-time prepack of canonical NVFP4 expert weights into the layout the
- * FFN calls read, and its exact inverse.  Canonical: codes [E, N, K/2] and
+ * FFN calls read, and its exact inverse (forum post "1x Spark GB10: 236B
+ * unpruned K-EXAONE-236B-A23B serving ...", the serving instructions that open
+ * it: the server's cold start is spent mostly on a one-time aligned repack of
+ * the loaded weights; here the repack is this call, run once per weight set).  Canonical: codes [E, N, K/2] and
  * scales [E, N, K/16], both row-major (the form nvfp4_quantize_act writes and
  * an NVFP4 checkpoint stores).  Packed: codes unchanged, scales in the tiled
  * order of the header comment over the E*N rows.  Bit-preserving, so
@@ -183,7 +188,10 @@ moe_status moe_nvfp4_unpack_weights(const uint8_t* packed_codes, const uint8_t* 
  * device FP32 [1]; weights in the layout of the header comment; h_gs [E]
  * FP32 (calibrated); expert_offsets [E+1] and sorted_pair_ids [T*k] from
  * moe_route; topk_w [T*k].  Requires H % 256 == 0, I % 128 == 0,
- * 1 <= k <= E <= 256.  workspace: moe_ffn_workspace_bytes(...) bytes,
+ * 1 <= k <= E <= 256; the kernels address operands with 32-bit byte offsets,
+ * so x codes (T*H/2 bytes), h codes (T*k*I/2 bytes) and one expert's w13 codes
+ * (I*H bytes) must each be under 4 GiB, and ceil(T*k/256) + E <= 65535
+ * (MOE_ERR_SHAPE otherwise).  workspace: moe_ffn_workspace_bytes(...) bytes,
  * 256-byte aligned; it holds the re-quantized h and the tile schedule.
  * Code arrays, activation scale arrays (x_scales, h_scales) and pair_out
  * must be 16-byte aligned, weight scale arrays 4-byte aligned.
@@ -326,7 +334,9 @@ moe_status moe_combine_block(const float* pair_out, const float* shared_out, int
  * x W^T unchanged in exact arithmetic.  src/dst [rows, cols] BF16 with row
  * strides ld_src/ld_dst (>= cols, multiples of 8); cols a multiple of 8, at
  * most 16384; src and dst 16-byte aligned and either identical (in place, same
- * stride) or not overlapping.  FP32 butterflies in a fixed order. */
+ * stride) or not overlapping.  FP64 butterflies in a fixed order (the ±1 sums of
+ * BF16 values are exact), one FP64 division by sqrt(b), then one rounding to
+ * BF16: the correctly rounded rotation. */
 moe_status hadamard_rotate_bf16(const uint16_t* src, int64_t rows, int64_t cols, int64_t ld_src,
                                 const float* signs, int64_t block, uint16_t* dst, int64_t ld_dst,
                                 void* stream);

@@ -88,6 +88,20 @@ moe_status check_ffn_shapes(int64_t T, int64_t H, int64_t E, int64_t I, int64_t 
   if (I <= 0 || I % 128 != 0) return fail(MOE_ERR_SHAPE, "I must be a positive multiple of 128 (got %lld)", (long long)I);
   if (k < 1 || E < k || E > 256) return fail(MOE_ERR_SHAPE, "need 1 <= k <= E <= 256 (k=%lld, E=%lld)", (long long)k, (long long)E);
   if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T*k must be < 2^31");
+  // The expert kernels address each operand with 32-bit byte offsets from a
+  // wave-uniform base: x codes by token (T*H/2 bytes), the h codes by sorted
+  // pair row (T*k*I/2 bytes), and each expert's weight codes from the expert's
+  // first row (I*H bytes for w13); the tile grid's y dimension is limited too.
+  const uint64_t lim = (uint64_t)1 << 32;
+  if ((uint64_t)T * (uint64_t)(H / 2) >= lim)
+    return fail(MOE_ERR_SHAPE, "x codes (T*H/2 = %llu bytes) must be under 4 GiB",
+                (unsigned long long)((uint64_t)T * (uint64_t)(H / 2)));
+  if ((uint64_t)(T * k) * (uint64_t)(I / 2) >= lim)
+    return fail(MOE_ERR_SHAPE, "h codes (T*k*I/2 = %llu bytes) must be under 4 GiB",
+                (unsigned long long)((uint64_t)(T * k) * (uint64_t)(I / 2)));
+  if ((uint64_t)I * (uint64_t)H >= lim) return fail(MOE_ERR_SHAPE, "one expert's w13 codes (I*H bytes) must be under 4 GiB");
+  if (moe::ffn_max_tiles(T, k, E) > 65535)
+    return fail(MOE_ERR_SHAPE, "too many m-tiles (%lld > 65535) for one launch", (long long)moe::ffn_max_tiles(T, k, E));
   return MOE_OK;
 }
 

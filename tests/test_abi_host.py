@@ -130,6 +130,29 @@ def test_ffn_validation(L):
     assert _ffn(L, T=0) == OK  # no pairs: no-op
 
 
+def test_ffn_rejects_shapes_past_32bit_offsets(L):
+    """The expert kernels address x codes (T*H/2 bytes), h codes (T*k*I/2 bytes) and one
+    expert's w13 codes (I*H bytes) with 32-bit offsets, and launch one grid row per m-tile:
+    shapes past those limits are rejected before anything is enqueued."""
+    big = 1 << 62
+    # largest legal x: T*H/2 just under 4 GiB at H = 6144 (k = 1 keeps h small)
+    t_max = ((1 << 32) - 1) // 3072
+    # (a legal shape stops at the missing workspace, checked after the shape: nothing is launched)
+    assert _ffn(L, T=t_max, H=6144, I=128, k=1, E=8, ws=None) == WORKSPACE
+    assert _ffn(L, T=t_max + 1, H=6144, I=128, k=1, E=8, wsb=big) == SHAPE
+    assert b"x codes" in L.moe_last_error()
+    # h codes: T*k*I/2 at I = 2048, k = 8 reaches 4 GiB at T*k = 4,194,304
+    assert _ffn(L, T=524287, H=256, I=2048, k=8, E=80, ws=None) == WORKSPACE
+    assert _ffn(L, T=524288, H=256, I=2048, k=8, E=80, wsb=big) == SHAPE
+    assert b"h codes" in L.moe_last_error()
+    # one expert's w13 codes: I*H bytes
+    assert _ffn(L, T=16, H=65536, I=65536, k=2, E=8, wsb=big) == SHAPE
+    g = L.moe_nvfp4_gate_up_swiglu
+    assert g(P, P, P, t_max + 1, 6144, P, P, P, P, 8, 128, 1, P, P, P, P, P2, big, None) == SHAPE
+    d = L.moe_nvfp4_down_scatter
+    assert d(P, P, P, 524288, 256, P, P, P, 80, 2048, 8, P, P, P, P, None, P2, big, None) == SHAPE
+
+
 def test_ffn_workspace_queries(L):
     full = L.moe_ffn_workspace_bytes(8192, 8, 80, 6144, 2048)
     stage = L.moe_ffn_stage_workspace_bytes(8192, 8, 80, 6144, 2048)
