@@ -7,10 +7,14 @@ quantization of the activations, gate_up + SwiGLU + re-quantization, down +
 weighted scatter with the per-pair sum of squares, the combine, and the REAP
 saliency finalize.  Inputs are resident in HBM before the timed region.
 
-Default workload: the decode-shaped layer (80 experts, top-8, hidden 6144,
-intermediate 2048, 16 tokens), HBM-bound.  Prints one JSON line.
+Default workload: the largest single-GPU one, the long batch with fused REAP
+saliency (80 experts, top-8, hidden 6144, intermediate 2048, 32768 tokens),
+MFMA-bound.  The same line carries, under "workloads", short measurements of
+the decode (HBM-bound, hot and with the last-level cache flushed between
+steps), Zipf-skewed prefill and 128-expert outlier workloads.  Prints one JSON
+line.
 
-  python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu-baseline] [--no-extra-workloads]
 """
 
 from __future__ import annotations
@@ -39,9 +43,16 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=1, help="workload index (0..4); 1 = decode-shaped layer")
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload index (0..4); 4 = long batch with fused REAP saliency, the largest")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the oracle's timed sample (default: 16 for the decode batch, 4 otherwise)")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the short measurements of the other full-size workloads")
+    ap.add_argument("--extra-steps", type=int, default=20, help="timed steps per extra workload")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="MiB written between decode steps for the cold (cache-flushed) measurement")
     ap.add_argument("--union-sweep", action="store_true",
                     help="decode only: time the layer on the first T tokens for T = 1, 2, 4, 8, 16 and report the "
                          "experts touched, weight bytes streamed and tokens/s (one JSON line)")
@@ -347,6 +358,147 @@ def cpu_baseline(cfg, n_tokens: int) -> dict:
                       f"{reps} pass{'es' if reps > 1 else ''} in {dt:.2f} s; offline RTN of the weights not timed; host CPU: {cpu}"}
 
 
+def layer_bytes_flops(cfg, counts):
+    """Algorithmic bytes and FLOPs of one whole-layer step: every touched expert's NVFP4 weights, the BF16
+    router, x in and y out (BF16); the FFN FLOPs (2 H 2I + 2 I H per pair) plus the router's 2 T H E."""
+    import numpy as np
+
+    touched = int(np.count_nonzero(counts))
+    nv = 0.5625
+    wbytes = touched * (3 * cfg.I * cfg.H * nv)
+    nbytes = wbytes + cfg.E * cfg.H * 2 + cfg.T * cfg.H * 2 + cfg.T * cfg.H * 2
+    flops = 2.0 * cfg.pairs * (cfg.H * 2 * cfg.I + cfg.I * cfg.H) + 2.0 * cfg.T * cfg.H * cfg.E
+    return dict(bytes=nbytes, flops=flops, touched=touched)
+
+
+def _roof(bound: str, work: float, seconds: float) -> dict:
+    if bound == "mfma":
+        a = work / seconds / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / MFMA_F16_PEAK_TFLOPS}
+    a = work / seconds / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
+
+
+def measure(cfg, layer, x, steps: int, warmup: int, reap: bool) -> dict:
+    """Time `steps` whole-layer steps (after `warmup` untimed ones) on the current stream.
+
+    The warm-up steps record HIP events around every stage (stage_ms_warmup) and pick the dominant FFN
+    stage; the timed steps record events only around that stage (each event adds a gap on the stream).
+    The timed region is bracketed by device synchronizations.  Returns the wall time per step, the
+    dominant kernel's mean event time and the routing counts of the last step."""
+    import numpy as np
+    import torch
+
+    stages = layer.STAGES
+    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(max(warmup, 1))]
+    for i in range(max(warmup, 1)):
+        layer(x, out_dtype=torch.bfloat16, reap=reap, events=wev[i])
+    torch.cuda.synchronize()
+    skip = min(2, len(wev) - 1)  # the first steps allocate and load
+    ms_stage = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in wev[skip:]])) for j, s in enumerate(stages)}
+    dom = "gate_up" if ms_stage["gate_up"] >= ms_stage["down"] else "down"
+    j_dom = stages.index(dom)
+    events = [[None] * (len(stages) + 1) for _ in range(steps)]
+    for ev in events:
+        ev[j_dom], ev[j_dom + 1] = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        out = layer(x, out_dtype=torch.bfloat16, reap=reap, events=events[i])
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    dom_ms = float(np.mean([ev[j_dom].elapsed_time(ev[j_dom + 1]) for ev in events]))
+    counts = out.route.expert_counts.cpu().numpy()
+    return dict(sec_per_step=sec, dom=dom, dom_ms=dom_ms, ms_stage=ms_stage, counts=counts)
+
+
+def roofline_of(cfg, m: dict) -> dict:
+    """The dominant kernel against its roofline (algorithmic work / its event time), the traffic the
+    committed counter summary gives for that kernel and workload, and the whole layer against the same
+    roofline on the wall clock of the timed steps."""
+    bf = stage_bytes_flops(cfg, m["counts"])
+    dom = m["dom"]
+    bound = "mfma" if cfg.bound == "mfma" else "hbm"
+    work = bf[dom]["flops"] if bound == "mfma" else bf[dom]["bytes"]
+    roof = _roof(bound, work, m["dom_ms"] / 1e3)
+    kernel = {"gate_up": "ffn_gate_up", "down": "ffn_down"}[dom]
+    roof["traffic"] = read_traffic(kernel, cfg.name)
+    roof["kernel"] = kernel
+    roof["kernel_ms"] = m["dom_ms"]
+    roof["algorithmic_bytes"] = bf[dom]["bytes"]
+    roof["algorithmic_flops"] = bf[dom]["flops"]
+    lb = layer_bytes_flops(cfg, m["counts"])
+    lw = lb["flops"] if bound == "mfma" else lb["bytes"]
+    layer_roof = _roof(bound, lw, m["sec_per_step"])
+    roof["layer"] = {"achieved": layer_roof["achieved"], "frac": layer_roof["frac"],
+                     "algorithmic_bytes" if bound == "hbm" else "algorithmic_flops": lw,
+                     "ms_per_step": m["sec_per_step"] * 1e3}
+    return roof
+
+
+def decode_cold_hot(cfg, layer, x, steps: int, warmup: int, flush_mib: int, reap: bool) -> dict:
+    """The decode layer per step (HIP events around each whole step), hot and with a flush_mib MiB buffer
+    written between steps so that no weight bytes stay in the last-level cache (256 MB on MI355X)."""
+    import numpy as np
+    import torch
+
+    scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=x.device)
+    res = {}
+    for mode in ("hot", "cold"):
+        for _ in range(warmup):
+            layer(x, out_dtype=torch.bfloat16, reap=reap)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            if mode == "cold":
+                scratch.fill_(float(i))
+            ev[i][0].record()
+            out = layer(x, out_dtype=torch.bfloat16, reap=reap)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        lb = layer_bytes_flops(cfg, out.route.expert_counts.cpu().numpy())
+        res[mode] = {"us_per_step_median": ms * 1e3, "tokens_per_s": cfg.T / (ms / 1e3),
+                     "hbm_frac": lb["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    res["flush_bytes"] = flush_mib * (1 << 20)
+    res["layer_bytes"] = lb["bytes"]
+    del scratch
+    return res
+
+
+def extra_workloads(main_cfg, main_layer, steps: int, warmup: int, flush_mib: int) -> dict:
+    """Short measurements of the other full-size workloads, each against its own roofline."""
+    import torch
+
+    from nvfp4_w4a4_mixture_amd import workload_io
+    from nvfp4_w4a4_mixture_amd.layer import NVFP4MoELayer
+    from workloads import CONFIGS, gen
+
+    out = {}
+    for cfg in CONFIGS[1:]:
+        if cfg.index == main_cfg.index:
+            continue
+        if cfg.weights == main_cfg.weights:  # the same expert weights: share them, with this workload's bias
+            bias = torch.from_numpy(gen.router_bias(cfg)).to(main_layer.device)
+            layer = NVFP4MoELayer(main_layer.w_router, bias, cfg.k, cfg.rsf, main_layer.x_gs, main_layer.h_gs,
+                                  *main_layer.w13, *main_layer.w2)
+        else:
+            layer, _ = workload_io.build_layer(cfg, main_layer.device)
+        x = workload_io.tokens(cfg, main_layer.device)
+        m = measure(cfg, layer, x, steps, warmup, reap=cfg.reap)
+        roof = roofline_of(cfg, m)
+        rec = {"workload": f"{cfg.name}: {cfg.describe()}", "reap": cfg.reap, "tokens_per_s": cfg.T / m["sec_per_step"],
+               "ms_per_step": m["sec_per_step"] * 1e3, "touched_experts": int((m["counts"] > 0).sum()),
+               "stage_ms_warmup": m["ms_stage"], "roofline": roof, "steps": steps, "warmup": warmup}
+        if cfg.name == "decode":
+            rec["per_step_events"] = decode_cold_hot(cfg, layer, x, steps, warmup, flush_mib, cfg.reap)
+        out[cfg.name] = rec
+        del layer, x
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -356,7 +508,6 @@ def main(argv=None) -> int:
         return 2
     if args.copy_probe:
         return copy_probe(args.copy_probe)
-    import numpy as np
     import torch
 
     from nvfp4_w4a4_mixture_amd import workload_io
@@ -369,7 +520,6 @@ def main(argv=None) -> int:
     x = workload_io.tokens(cfg, dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
-    stages = layer.STAGES
     if args.union_sweep:
         print(json.dumps(union_sweep(cfg, layer, x, args.steps, args.warmup)), flush=True)
         return 0
@@ -384,60 +534,17 @@ def main(argv=None) -> int:
         print(json.dumps(reap_prune_study(cfg, layer, x, args.reap_prune, args.steps, args.warmup)), flush=True)
         return 0
 
-    # warm-up steps, with events around every stage: the per-stage breakdown and the dominant FFN stage
-    wev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(max(args.warmup, 1))]
-    for i in range(max(args.warmup, 1)):
-        layer(x, out_dtype=torch.bfloat16, reap=True, events=wev[i])
-    torch.cuda.synchronize()
-    skip = min(2, len(wev) - 1)  # the first steps allocate and load
-    ms_stage = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in wev[skip:]])) for j, s in enumerate(stages)}
-    dom = "gate_up" if ms_stage["gate_up"] >= ms_stage["down"] else "down"
-    j_dom = stages.index(dom)
-    # timed steps: events only around the dominant kernel's stage (each extra event adds a gap on the stream)
-    events = [[None] * (len(stages) + 1) for _ in range(args.steps)]
-    for ev in events:
-        ev[j_dom], ev[j_dom + 1] = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        out = layer(x, out_dtype=torch.bfloat16, reap=True, events=events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sec = t1 - t0
-    dom_ms = float(np.mean([ev[j_dom].elapsed_time(ev[j_dom + 1]) for ev in events]))
-    counts = out.route.expert_counts.cpu().numpy()
-    bf = stage_bytes_flops(cfg, counts)
-    dom_s = dom_ms / 1e3
-    workload = cfg.name
-    kernel = {"gate_up": "ffn_gate_up", "down": "ffn_down"}[dom]
-    if cfg.bound == "mfma":
-        achieved = bf[dom]["flops"] / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_F16_PEAK_TFLOPS}
-    else:
-        achieved = bf[dom]["bytes"] / dom_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
-    roof["traffic"] = read_traffic(kernel, workload)
-    roof["kernel"] = kernel
-    roof["kernel_ms"] = dom_ms
-    roof["algorithmic_bytes"] = bf[dom]["bytes"]
-    roof["algorithmic_flops"] = bf[dom]["flops"]
-    # the whole FFN (both stages) against the same roofline, for context
-    ffn_s = (ms_stage["gate_up"] + ms_stage["down"]) / 1e3
-    if cfg.bound == "mfma":
-        roof["ffn_frac_warmup"] = (bf["gate_up"]["flops"] + bf["down"]["flops"]) / ffn_s / 1e12 / MFMA_F16_PEAK_TFLOPS
-    else:
-        roof["ffn_frac_warmup"] = (bf["gate_up"]["bytes"] + bf["down"]["bytes"]) / ffn_s / 1e9 / HBM_PEAK_GBS
-
+    # the headline: every step runs the whole layer with the REAP saliency
+    m = measure(cfg, layer, x, args.steps, args.warmup, reap=True)
+    roof = roofline_of(cfg, m)
     rec = {
         "metric": METRIC,
-        "value": cfg.T * args.steps / sec,
+        "value": cfg.T / m["sec_per_step"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": sec * 1e3 / args.steps,
+        "ms_per_step": m["sec_per_step"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -447,13 +554,21 @@ def main(argv=None) -> int:
                                f"routed_scaling_factor {cfg.rsf}, REAP saliency every step",
                    "operands": "nvfp4 codes decoded in registers to f16 for MFMA, f32 accumulate; routing in f64",
                    "tokens_per_step": cfg.T, "experts": cfg.E, "top_k": cfg.k, "hidden": cfg.H,
-                   "intermediate": cfg.I, "touched_experts": bf["touched"]},
-        "stage_ms_warmup": ms_stage,
+                   "intermediate": cfg.I, "touched_experts": int((m["counts"] > 0).sum())},
+        "stage_ms_warmup": m["ms_stage"],
         "roofline": roof,
         "setup_s": round(setup_s, 1),
     }
+    print(f"# headline done: {rec['value']:.0f} tokens/s, {rec['ms_per_step']:.3f} ms/step", file=sys.stderr,
+          flush=True)
+    if not args.no_extra_workloads:
+        rec["workloads"] = extra_workloads(cfg, layer, args.extra_steps, min(args.warmup, 5), args.flush_mib)
+        print("# extra workloads done", file=sys.stderr, flush=True)
+    del layer, x
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
+        n = args.cpu_tokens or (16 if cfg.T <= 16 else 4)
+        rec["cpu_baseline"] = cpu_baseline(cfg, min(n, cfg.T))
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -62,3 +62,29 @@ def test_traffic_summary_only_for_its_own_kernel_source(bench, tmp_path, monkeyp
     assert bench.read_traffic("ffn_gate_up", "decode") is None
     # and a missing summary gives none either
     assert bench.read_traffic("ffn_down", "nonexistent") is None
+
+
+def test_layer_bytes_and_flops(bench):
+    """Whole-layer work of one step: touched experts' weights + router + x + y; FFN + router FLOPs."""
+    from workloads import by_name
+
+    cfg = by_name("long_reap")
+    counts = np.ones(cfg.E, dtype=np.int64)
+    r = bench.layer_bytes_flops(cfg, counts)
+    assert r["touched"] == 80
+    assert r["flops"] == cfg.pairs * 75_497_472 + 2 * cfg.T * cfg.H * cfg.E
+    assert r["bytes"] == 80 * 21_233_664 + cfg.E * cfg.H * 2 + 2 * cfg.T * cfg.H * 2
+    # the roofline record: mfma work over seconds against the 2.5 PFLOP/s FP16 peak
+    roof = bench._roof("mfma", 2.5e15, 1.0)
+    assert roof["unit"] == "TFLOP/s" and abs(roof["frac"] - 1.0) < 1e-12
+    roof = bench._roof("hbm", 4e12, 1.0)
+    assert roof["unit"] == "GB/s" and abs(roof["frac"] - 0.5) < 1e-12
+
+
+def test_default_workload_is_the_largest(bench):
+    from workloads import CONFIGS
+
+    args = bench.parse_args([])
+    assert CONFIGS[args.config].name == "long_reap"
+    assert CONFIGS[args.config].T == max(c.T for c in CONFIGS)
+    assert bench.main(["--gpus", "2"]) == 2  # several GPUs: refused with a message
