@@ -62,7 +62,7 @@ moe_status launched(hipError_t e, const char* what) {
 
 // ---- FFN workspace layout
 struct FfnWs {
-  size_t tile_info, sq_part, h_codes, h_scales, total_stage, total_full;
+  size_t tile_info, spill_row, sq_part, h_codes, h_scales, total_stage, total_full;
 };
 
 FfnWs ffn_ws_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
@@ -71,6 +71,8 @@ FfnWs ffn_ws_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
   size_t o = 0;
   w.tile_info = o;
   o = round_up(o + (size_t)tiles * 16, 256);
+  w.spill_row = o;
+  o = round_up(o + (size_t)H * 4, 256);
   w.sq_part = o;
   o = round_up(o + (size_t)(T * k) * (size_t)moe::ffn_sq_parts(H) * 4, 256);
   w.total_stage = o;
@@ -263,6 +265,7 @@ static moe_status down_impl(const uint8_t* h_codes, const uint8_t* h_scales, con
   a.tile_info = reinterpret_cast<const int32_t*>(ws + L.tile_info);
   a.pair_out = pair_out;
   a.sq_part = pair_sqnorm ? reinterpret_cast<float*>(ws + L.sq_part) : nullptr;
+  a.spill_row = reinterpret_cast<float*>(ws + L.spill_row);
   a.n_part = moe::ffn_use_small(T) ? (int)(H / 64) : (int)(H / moe::ffn_tiled_bn());
   if (moe_status s = launched(moe::launch_ffn_stage(1, a, T, E, build_schedule, st), "moe_nvfp4_down_scatter"))
     return s;
@@ -318,28 +321,33 @@ moe_status moe_nvfp4_down_scatter(const uint8_t* h_codes, const uint8_t* h_scale
                    /*build_schedule=*/true, (hipStream_t)stream);
 }
 
-moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
-                                 int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
-                                 const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
-                                 const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
-                                 const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
-                                 float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
+// Validation shared by moe_nvfp4_grouped_ffn and its static-scratch variant.
+static moe_status check_grouped_ffn(const char* fn, const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                    int64_t T, int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                    const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                    const float* w2_gs, const float* h_gs, int64_t E, int64_t I, int64_t k,
+                                    const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                                    const float* topk_w, const float* pair_out) {
   if (moe_status s = check_ffn_shapes(T, H, E, I, k)) return s;
   if (T == 0) return MOE_OK;  // zero-size arrays may be NULL
   if (!x_codes || !x_scales || !x_gs || !w13_codes || !w13_scales || !w13_gs || !w2_codes || !w2_scales || !w2_gs ||
       !h_gs || !expert_offsets || !sorted_pair_ids || !topk_w || !pair_out)
-    return fail(MOE_ERR_NULL, "moe_nvfp4_grouped_ffn: a required pointer is NULL");
+    return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) ||
       !aligned(x_scales, 16) || !aligned(w13_scales, 4) || !aligned(w2_scales, 4))
-    return fail(MOE_ERR_ALIGN,
-                "moe_nvfp4_grouped_ffn: code arrays, x_scales and pair_out must be 16-byte, weight scales 4-byte aligned");
+    return fail(MOE_ERR_ALIGN, "%s: code arrays, x_scales and pair_out must be 16-byte, weight scales 4-byte aligned",
+                fn);
+  return MOE_OK;
+}
+
+// Both stages in one workspace `ws` of at least ffn_ws_layout(...).total_full bytes.
+static moe_status grouped_ffn_impl(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
+                                   int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                                   const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                                   const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
+                                   const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
+                                   float* pair_sqnorm, unsigned char* ws, hipStream_t st) {
   const FfnWs L = ffn_ws_layout(T, k, E, H, I);
-  if (!workspace || workspace_bytes < L.total_full)
-    return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_grouped_ffn: workspace needs %zu bytes", L.total_full);
-  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if (moe_status s = check_device()) return s;
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  hipStream_t st = (hipStream_t)stream;
   uint8_t* h_codes = ws + L.h_codes;
   uint8_t* h_scales = ws + L.h_scales;
   if (moe_status s = gate_up_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, h_gs, E, I, k,
@@ -348,6 +356,28 @@ moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales
   // stage 2 reuses the schedule stage 1 built in the same workspace
   return down_impl(h_codes, h_scales, h_gs, T, H, w2_codes, w2_scales, w2_gs, E, I, k, expert_offsets,
                    sorted_pair_ids, topk_w, pair_out, pair_sqnorm, ws, /*build_schedule=*/false, st);
+}
+
+moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
+                                 int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+                                 const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+                                 const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
+                                 const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
+                                 float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "moe_nvfp4_grouped_ffn";
+  if (moe_status s = check_grouped_ffn(fn, x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes,
+                                       w2_scales, w2_gs, h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w,
+                                       pair_out))
+    return s;
+  if (T == 0) return MOE_OK;
+  const FfnWs L = ffn_ws_layout(T, k, E, H, I);
+  if (!workspace || workspace_bytes < L.total_full)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, L.total_full);
+  if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (moe_status s = check_device()) return s;
+  return grouped_ffn_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs,
+                          h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_sqnorm,
+                          static_cast<unsigned char*>(workspace), (hipStream_t)stream);
 }
 
 moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y,

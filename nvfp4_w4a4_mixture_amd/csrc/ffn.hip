@@ -598,42 +598,15 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     __syncthreads();
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
     const int64_t col0 = (int64_t)((WIDE && wm) ? nt2 : nt) * Tiled::BN + 128 * wn;  // this wave's first column
-    // v[16 i + q]: this lane's sum of f^2 over its 4 columns of row (i, q)
-    float v[64];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int qh = 0; qh < 4; ++qh) {
-        // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
-        const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
-        const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
-        const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const int q = 4 * qh + qq, row = rb + qq;
-          const bool ok = row < rows_here;
-          const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
-          const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
-          float ss = 0.0f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float f = acc[i][j][q] * alpha;
-            ss += f * f;
-            // written once and read once by the combine: non-temporal, so the
-            // weighted rows do not push the operand tiles out of L2
-            if (ok) __builtin_nontemporal_store(wp * f, &a.pair_out[p * a.H + col0 + 32 * j + r]);
-          }
-          v[16 * i + q] = ss;
-        }
-      }
-    }
-    // Sum each row's partials over the 32 lanes of the half-wave with a
-    // transposed butterfly: at each level a lane keeps half of its remaining
-    // rows and sends the other half to its partner (lane ^ mask), so the
-    // shuffles of a level are independent.  The masks go 1, 2, 8 (in-register
-    // DPP moves: 56 of the 62 shuffles) and then 4, 16 (LDS swizzles).  Lane r
-    // then holds the sums of rows 16 i + q = k + 32 r0 + 16 r1 + 8 r3 + 4 r2 +
-    // 2 r4 (r_b: bit b of r), k = 0, 1.  The order is fixed: deterministic.
+    // Sum each row's f^2 over the 32 lanes of the half-wave with a transposed
+    // butterfly, two 32-row blocks (i = 2 ii, 2 ii + 1) at a time so that only
+    // 32 partials are live beside the accumulators: at each level a lane keeps
+    // half of its remaining rows and sends the other half to its partner
+    // (lane ^ mask), so the shuffles of a level are independent.  The masks go
+    // 1, 2, 8 (in-register DPP moves: 28 of the 31 shuffles of a pair) and then
+    // 4, 16 (LDS swizzles).  Lane r then holds the sum of row 16 il + q =
+    // 16 r0 + 8 r1 + 4 r3 + 2 r2 + r4 of the pair (r_b: bit b of r).  The order
+    // is fixed: deterministic.
     auto xshfl = [](float x, int mask) -> float {
       const int xi = __float_as_int(x);
       int y;
@@ -644,25 +617,61 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
       else y = __builtin_amdgcn_ds_swizzle(xi, 0x401F);                              // xor 16 within 32 lanes
       return __int_as_float(y);
     };
-    constexpr int kMask[5] = {1, 2, 8, 4, 16};
-#pragma unroll
-    for (int lvl = 0; lvl < 5; ++lvl) {
-      const int mask = kMask[lvl], half = 32 >> lvl;
-      const bool up = (r & mask) != 0;
-#pragma unroll
-      for (int k = 0; k < half; ++k) {
-        const float send = up ? v[k] : v[k + half];
-        const float keep = up ? v[k + half] : v[k];
-        v[k] = keep + xshfl(send, mask);
-      }
-    }
     // full tiles: sqbuf[wn][row]; wide tiles: sqbuf[wm][wn][row], wm = the n-tile
     float* sqw = sqbuf + (WIDE ? wm * 256 + wn * 128 : wn * 256);
-    const int rbase = 32 * (r & 1) + 16 * ((r >> 1) & 1) + 8 * ((r >> 3) & 1) + 4 * ((r >> 2) & 1) + 2 * (r >> 4);
+    const int lrow = 16 * (r & 1) + 8 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1) + 2 * ((r >> 2) & 1) + (r >> 4);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int idx = rbase + k, i = idx >> 4, q = idx & 15;
-      sqw[a_row0 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[k];
+    for (int ii = 0; ii < 2; ++ii) {
+      // v[16 il + q]: this lane's sum of f^2 over its 4 columns of row (i = 2 ii + il, q)
+      float v[32];
+#pragma unroll
+      for (int il = 0; il < 2; ++il) {
+        const int i = 2 * ii + il;
+#pragma unroll
+        for (int qh = 0; qh < 4; ++qh) {
+          // one group of four rows at a time: their 16 store addresses are not
+          // all computed ahead (that ran out of registers and spilled)
+          __builtin_amdgcn_sched_barrier(0);
+          // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
+          const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
+          const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
+          const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int q = 4 * qh + qq, row = rb + qq;
+            const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
+            const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
+            // rows past the tile's last pair store to the workspace's spill row
+            // instead of branching: the epilogue stays one straight block, so
+            // the accumulators are read out group by group
+            float* dst = (row < rows_here ? a.pair_out + p * a.H : a.spill_row) + col0 + r;
+            float ss = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float f = acc[i][j][q] * alpha;
+              ss += f * f;
+              // written once and read once by the combine: non-temporal, so the
+              // weighted rows do not push the operand tiles out of L2
+              __builtin_nontemporal_store(wp * f, dst + 32 * j);
+            }
+            v[16 * il + q] = ss;
+          }
+        }
+      }
+      constexpr int kMask[5] = {1, 2, 8, 4, 16};
+#pragma unroll
+      for (int lvl = 0; lvl < 5; ++lvl) {
+        const int mask = kMask[lvl], half = 16 >> lvl;
+        const bool up = (r & mask) != 0;
+#pragma unroll
+        for (int k = 0; k < half; ++k) {
+          const float send = up ? v[k] : v[k + half];
+          const float keep = up ? v[k + half] : v[k];
+          v[k] = keep + xshfl(send, mask);
+        }
+      }
+      const int i = 2 * ii + (lrow >> 4), q = lrow & 15;
+      sqw[a_row0 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[0];
     }
     __syncthreads();
     if (a.sq_part != nullptr) {
