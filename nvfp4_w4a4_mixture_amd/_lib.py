@@ -13,7 +13,9 @@ import os
 
 import torch  # noqa: F401  (loads the HIP runtime first)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_nvfp4.so")
+# MOE_NVFP4_LIB selects another build of the same library (the host-sanitized one, for example)
+LIB_PATH = os.environ.get("MOE_NVFP4_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                           "libmoe_nvfp4.so")
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_WORKSPACE",

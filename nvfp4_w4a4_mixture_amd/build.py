@@ -32,28 +32,41 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+# Host-code sanitizers for a checking build (AddressSanitizer + UndefinedBehaviorSanitizer).  Each
+# flag is applied to the host compilation only; device code is built exactly as in the product.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+
+
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=(), extra=()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *[f"-D{d}" for d in defines], *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, out_dir: str = OUT_DIR, build_dir: str = BUILD_DIR, defines=()) -> str:
+def build(verbose: bool = False, out_dir: str = OUT_DIR, build_dir: str = BUILD_DIR, defines=(),
+          sanitize: bool = False) -> str:
     """Compile every source and link ``<out_dir>/libmoe_nvfp4.so``; returns its path.
 
-    ``defines`` (NAME=VALUE strings) override compile-time tile parameters."""
+    ``defines`` (NAME=VALUE strings) override compile-time tile parameters.  ``sanitize``
+    instruments the host code with AddressSanitizer and UndefinedBehaviorSanitizer (the library
+    then needs the ASan runtime preloaded); by default it goes to ``_build/sanitize/``."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
+    if sanitize and out_dir == OUT_DIR:
+        out_dir = build_dir = SANITIZE_DIR
+    extra = SANITIZE_HOST if sanitize else []
     os.makedirs(build_dir, exist_ok=True)
     os.makedirs(out_dir, exist_ok=True)
     with ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines, extra), SOURCES))
     tmp = os.path.join(out_dir, LIB_NAME + ".tmp")
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -64,6 +77,15 @@ def build(verbose: bool = False, out_dir: str = OUT_DIR, build_dir: str = BUILD_
     return out
 
 
+def asan_runtime() -> str:
+    """Path of the ASan runtime matching hipcc (preloaded to run a sanitized build)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError(f"ASan runtime not found (hipcc said {path!r})")
+    return path
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)
