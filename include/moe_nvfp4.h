@@ -192,9 +192,8 @@ moe_status moe_nvfp4_unpack_weights(const uint8_t* packed_codes, const uint8_t* 
  * so x codes (T*H/2 bytes), h codes (T*k*I/2 bytes) and one expert's w13 codes
  * (I*H bytes) must each be under 4 GiB, and ceil(T*k/256) + E <= 65535
  * (MOE_ERR_SHAPE otherwise).  workspace: moe_ffn_workspace_bytes(...) bytes,
- * 256-byte aligned; it holds the re-quantized h, the tile schedule, the
- * per-tile partial sums of f^2 and one row that stores of a tile's rows past
- * its last pair go to.
+ * 256-byte aligned; it holds the re-quantized h, the tile schedule and the
+ * per-tile partial sums of f^2.
  * Code arrays, activation scale arrays (x_scales, h_scales) and pair_out
  * must be 16-byte aligned, weight scale arrays 4-byte aligned.
  * Pairs not listed in sorted_pair_ids are not written. */

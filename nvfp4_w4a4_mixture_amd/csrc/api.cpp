@@ -62,7 +62,7 @@ moe_status launched(hipError_t e, const char* what) {
 
 // ---- FFN workspace layout
 struct FfnWs {
-  size_t tile_info, spill_row, sq_part, h_codes, h_scales, total_stage, total_full;
+  size_t tile_info, sq_part, h_codes, h_scales, total_stage, total_full;
 };
 
 FfnWs ffn_ws_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
@@ -71,8 +71,6 @@ FfnWs ffn_ws_layout(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I) {
   size_t o = 0;
   w.tile_info = o;
   o = round_up(o + (size_t)tiles * 16, 256);
-  w.spill_row = o;
-  o = round_up(o + (size_t)H * 4, 256);
   w.sq_part = o;
   o = round_up(o + (size_t)(T * k) * (size_t)moe::ffn_sq_parts(H) * 4, 256);
   w.total_stage = o;
@@ -265,7 +263,6 @@ static moe_status down_impl(const uint8_t* h_codes, const uint8_t* h_scales, con
   a.tile_info = reinterpret_cast<const int32_t*>(ws + L.tile_info);
   a.pair_out = pair_out;
   a.sq_part = pair_sqnorm ? reinterpret_cast<float*>(ws + L.sq_part) : nullptr;
-  a.spill_row = reinterpret_cast<float*>(ws + L.spill_row);
   a.n_part = moe::ffn_use_small(T) ? (int)(H / 64) : (int)(H / moe::ffn_tiled_bn());
   if (moe_status s = launched(moe::launch_ffn_stage(1, a, T, E, build_schedule, st), "moe_nvfp4_down_scatter"))
     return s;

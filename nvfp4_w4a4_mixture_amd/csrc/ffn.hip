@@ -302,7 +302,8 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
   using S = TileShape<WIDE>;
   constexpr int NS = S::NS;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in scalar registers
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   // this wave's first A row and first B row inside the tile
@@ -585,6 +586,10 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
       a.h_scales[hrow * (a.I / 16) + hcol / 16] = (uint8_t)sc;
     }
   } else {
+    // The lane's column r and row half g again, from the hardware lane id:
+    // values derived from threadIdx.x at the top would be held across the loop.
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int r = lane_e & 31, g = lane_e >> 5;
     // Σf² partials [n-tile half][wn][128 rows] (full tiles: [wn][256 rows])
     float* sqbuf = reinterpret_cast<float*>(smem + (Tiled::kLds - Tiled::kSqBytes));
     // the tile's pair ids and weights, staged once in the (now free) ring
@@ -629,9 +634,6 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
         const int i = 2 * ii + il;
 #pragma unroll
         for (int qh = 0; qh < 4; ++qh) {
-          // one group of four rows at a time: their 16 store addresses are not
-          // all computed ahead (that ran out of registers and spilled)
-          __builtin_amdgcn_sched_barrier(0);
           // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
           const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
           const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
@@ -641,18 +643,21 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
             const int q = 4 * qh + qq, row = rb + qq;
             const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
             const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
-            // rows past the tile's last pair store to the workspace's spill row
-            // instead of branching: the epilogue stays one straight block, so
-            // the accumulators are read out group by group
-            float* dst = (row < rows_here ? a.pair_out + p * a.H : a.spill_row) + col0 + r;
-            float ss = 0.0f;
+            // one bounds branch per row around its four stores (a branch per
+            // store made the compiler copy every accumulator out of the AGPRs
+            // ahead of the first one, and spill)
+            float* dst = a.pair_out + p * a.H + col0 + r;
+            float ss = 0.0f, fv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float f = acc[i][j][q] * alpha;
-              ss += f * f;
+              fv[j] = acc[i][j][q] * alpha;
+              ss += fv[j] * fv[j];
+            }
+            if (row < rows_here) {
               // written once and read once by the combine: non-temporal, so the
               // weighted rows do not push the operand tiles out of L2
-              __builtin_nontemporal_store(wp * f, dst + 32 * j);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(wp * fv[j], dst + 32 * j);
             }
             v[16 * il + q] = ss;
           }

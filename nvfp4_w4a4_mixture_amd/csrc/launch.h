@@ -51,7 +51,6 @@ struct FfnArgs {
   uint8_t* h_scales;
   float* pair_out;  // down outputs
   float* sq_part;   // [T*k, n_part] partial sums of f^2, or null
-  float* spill_row;  // down (tiled): [H] workspace row that a tile's rows past its last pair write to
   int n_part;
 };
 
