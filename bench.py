@@ -439,11 +439,12 @@ def roofline_of(cfg, m: dict) -> dict:
 
 def decode_cold_hot(cfg, layer, x, steps: int, warmup: int, flush_mib: int, reap: bool) -> dict:
     """The decode layer per step (HIP events around each whole step), hot and with a flush_mib MiB buffer
-    written between steps so that no weight bytes stay in the last-level cache (256 MB on MI355X)."""
+    read between steps so that no weight bytes stay in the last-level cache (256 MB on MI355X).  The
+    flush reads (a sum) rather than writes, so no dirty lines are left to write back during the step."""
     import numpy as np
     import torch
 
-    scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=x.device)
+    scratch = torch.ones(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=x.device)
     res = {}
     for mode in ("hot", "cold"):
         for _ in range(warmup):
@@ -452,7 +453,7 @@ def decode_cold_hot(cfg, layer, x, steps: int, warmup: int, flush_mib: int, reap
         torch.cuda.synchronize()
         for i in range(steps):
             if mode == "cold":
-                scratch.fill_(float(i))
+                scratch.sum()
             ev[i][0].record()
             out = layer(x, out_dtype=torch.bfloat16, reap=reap)
             ev[i][1].record()
