@@ -225,6 +225,25 @@ moe_status moe_nvfp4_down_scatter(
     int64_t k, const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
     float* pair_out, float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_nvfp4_grouped_ffn for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and requirements
+ * as moe_nvfp4_grouped_ffn, without the workspace: the library's own static
+ * scratch array of MOE_NVFP4_STATIC_SCRATCH_BYTES per device (held until the
+ * process ends) takes its place, and the call allocates nothing.  Shapes whose
+ * moe_ffn_workspace_bytes(T, k, E, H, I) exceeds that size are rejected with
+ * MOE_ERR_SHAPE (at H 6144, I 2048, top-8: up to about 2,700 tokens).  Every
+ * call on one device shares that device's array: calls that overlap in time on
+ * one device (other streams, other host threads) race and must not be made. */
+#define MOE_NVFP4_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+moe_status moe_nvfp4_grouped_ffn_noalloc(
+    const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T, int64_t H,
+    const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
+    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
+    const float* h_gs, int64_t E, int64_t I, int64_t k,
+    const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
+    float* pair_out, float* pair_sqnorm, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Weighted combine: y[t, :] = sum_{j=0..k-1} pair_out[t*k + j, :], summed in
  * j order (deterministic).  pair_out already carries the routing weight

@@ -41,6 +41,8 @@ SIGNATURES = {
     "moe_ffn_stage_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "moe_nvfp4_grouped_ffn": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
                                      _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "moe_nvfp4_grouped_ffn_noalloc": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
+                                             _p, _p, _p, _p, _p, _p]),
     "moe_nvfp4_gate_up_swiglu": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p,
                                         _p, _p, _p, _sz, _p]),
     "moe_nvfp4_down_scatter": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p,

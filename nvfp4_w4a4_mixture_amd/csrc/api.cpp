@@ -377,6 +377,68 @@ moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales
                           static_cast<unsigned char*>(workspace), (hipStream_t)stream);
 }
 
+// ---- the grouped FFN on a static scratch array: allocates nothing
+
+}  // extern "C"
+
+namespace {
+
+// The FFN workspace of the no-allocation entry point: one array per device,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: only its device address, from
+// hipGetSymbolAddress, is ever passed to a kernel.
+constexpr size_t kStaticScratchBytes = MOE_NVFP4_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};  // device address of `scratch` per device id
+
+// The current device's copy of `scratch`, looked up once per device with that device current.
+moe_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return fail(MOE_ERR_DEVICE, "no current HIP device");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_nvfp4_grouped_ffn_noalloc(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs,
+                                         int64_t T, int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales,
+                                         const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                         const float* w2_gs, const float* h_gs, int64_t E, int64_t I, int64_t k,
+                                         const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
+                                         const float* topk_w, float* pair_out, float* pair_sqnorm, void* stream) {
+  const char* fn = "moe_nvfp4_grouped_ffn_noalloc";
+  if (moe_status s = check_grouped_ffn(fn, x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes,
+                                       w2_scales, w2_gs, h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w,
+                                       pair_out))
+    return s;
+  if (T == 0) return MOE_OK;
+  const FfnWs L = ffn_ws_layout(T, k, E, H, I);
+  if (L.total_full > kStaticScratchBytes)
+    return fail(MOE_ERR_SHAPE, "%s: this shape needs %zu bytes of scratch; the static scratch holds %zu", fn,
+                L.total_full, kStaticScratchBytes);
+  if (moe_status s = check_device()) return s;
+  void* ws = nullptr;
+  if (moe_status s = static_scratch(&ws)) return s;
+  // nothing in the workspace needs to start at zero: the schedule is rebuilt and
+  // every h row and partial sum is written before it is read
+  return grouped_ffn_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs,
+                          h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_sqnorm,
+                          static_cast<unsigned char*>(ws), (hipStream_t)stream);
+}
+
 moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y,
                        void* stream) {
   if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))

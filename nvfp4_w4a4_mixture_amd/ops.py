@@ -16,7 +16,7 @@ import torch
 from ._lib import MoEError, check, lib  # noqa: F401
 
 __all__ = ["moe_route", "moe_route_quantize", "nvfp4_quantize_act", "nvfp4_quantize_weights", "moe_nvfp4_grouped_ffn",
-           "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
+           "moe_nvfp4_grouped_ffn_noalloc", "moe_nvfp4_gate_up_swiglu", "moe_nvfp4_down_scatter", "moe_combine", "reap_saliency",
            "moe_combine_reap", "reap_prune_select", "moe_gather_experts", "moe_shared_workspace_bytes", "moe_shared_expert",
            "moe_shared_gate_up", "moe_shared_down", "moe_combine_block", "hadamard_rotate_bf16",
            "moe_nvfp4_prepack_weights", "moe_nvfp4_unpack_weights",
@@ -211,6 +211,36 @@ def moe_nvfp4_grouped_ffn(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs
                                      _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w), _p(pair_out),
                                      _p(pair_sqnorm), _p(ws), ws.numel(), _stream(stream))
     check(st, "moe_nvfp4_grouped_ffn")
+    return pair_out, pair_sqnorm
+
+
+def moe_nvfp4_grouped_ffn_noalloc(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales,
+                                  w2_gs, h_gs, k: int, expert_offsets, sorted_pair_ids, topk_w, pair_out,
+                                  pair_sqnorm: Optional[torch.Tensor] = None, stream=None):
+    """moe_nvfp4_grouped_ffn on the library's static scratch: the caller passes every output
+    (nothing is allocated here or in the library, so the call can be captured in a graph)."""
+    T, H, E, I = _ffn_dims(x_codes, w13_codes, w2_codes)
+    _need(x_codes, "x_codes", torch.uint8, (T, H // 2))
+    _need(x_scales, "x_scales", torch.uint8, (T, H // 16))
+    _need(x_gs, "x_gs", torch.float32, (1,))
+    _need(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, H // 2))
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I // 16, H // 128, 16, 8))
+    _need(w13_gs, "w13_gs", torch.float32, (E, 2))
+    _need(w2_codes, "w2_codes", torch.uint8, (E, H, I // 2))
+    _need(w2_scales, "w2_scales", torch.uint8, (E, H // 16, I // 128, 16, 8))
+    _need(w2_gs, "w2_gs", torch.float32, (E,))
+    _need(h_gs, "h_gs", torch.float32, (E,))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _need(sorted_pair_ids, "sorted_pair_ids", torch.int32, (T * k,))
+    _need(topk_w, "topk_w", torch.float32)
+    _need(pair_out, "pair_out", torch.float32, (T * k, H))
+    if pair_sqnorm is not None:
+        _need(pair_sqnorm, "pair_sqnorm", torch.float32, (T * k,))
+    st = lib().moe_nvfp4_grouped_ffn_noalloc(_p(x_codes), _p(x_scales), _p(x_gs), T, H, _p(w13_codes),
+                                             _p(w13_scales), _p(w13_gs), _p(w2_codes), _p(w2_scales), _p(w2_gs),
+                                             _p(h_gs), E, I, k, _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w),
+                                             _p(pair_out), _p(pair_sqnorm), _stream(stream))
+    check(st, "moe_nvfp4_grouped_ffn_noalloc")
     return pair_out, pair_sqnorm
 
 

@@ -153,6 +153,24 @@ def test_ffn_rejects_shapes_past_32bit_offsets(L):
     assert d(P, P, P, 524288, 256, P, P, P, 80, 2048, 8, P, P, P, P, None, P2, big, None) == SHAPE
 
 
+def test_noalloc_ffn_validation(L):
+    """The static-scratch FFN: same checks as the workspace call, and shapes whose workspace
+    exceeds the static scratch are rejected before anything is enqueued."""
+    f = L.moe_nvfp4_grouped_ffn_noalloc
+
+    def call(T=16, H=256, E=8, I=128, k=2, xc=P, po=P):
+        return f(xc, P, P, T, H, P, P, P, P, P, P, P, E, I, k, P, P, P, po, None, None)
+
+    assert call(xc=None) == NULL
+    assert call(H=200) == SHAPE
+    assert call(xc=ctypes.c_void_p(0x10008)) == ALIGN
+    assert call(T=0) == OK
+    scratch = 32 << 20
+    assert L.moe_ffn_workspace_bytes(8192, 8, 80, 6144, 2048) > scratch
+    assert call(T=8192, H=6144, E=80, I=2048, k=8) == SHAPE
+    assert b"static scratch" in L.moe_last_error()
+
+
 def test_ffn_workspace_queries(L):
     full = L.moe_ffn_workspace_bytes(8192, 8, 80, 6144, 2048)
     stage = L.moe_ffn_stage_workspace_bytes(8192, 8, 80, 6144, 2048)
