@@ -254,11 +254,12 @@ void ffn_small_kernel(FfnArgs a) {
 // Four waves, each owning a 128 x 128 block of 16 accumulator tiles.  A full
 // tile is 256 pair rows x 256 weight rows (waves 2 x 2).  An expert's last
 // m-tile with at most 128 rows is run wide instead: 128 pair rows x 512 weight
-// rows (n-tiles nt and nt + gx / 2, waves 1 x 4 over the weight rows), and the
-// workgroups of the second half of the n-tiles exit, so no MFMA work goes to
-// the empty half.  Pairing nt with nt + gx / 2 rather than nt + 1 keeps the
-// running workgroups spread over all XCDs (workgroups go to the XCDs in turn
-// by linear id).
+// rows (n-tile nt and a partner n-tile, waves 1 x 4 over the weight rows), and
+// the workgroups of the partner n-tiles exit, so no MFMA work goes to the
+// empty half.  Workgroups go to the 8 XCDs in turn by linear id; the partner
+// is chosen so that the working workgroups stay spread over all XCDs: with the
+// XCD-aware tile order (a multiple of 8 n-tiles) it is the n-tile half a
+// quarter away inside the same XCD's quarter, otherwise nt + gx / 2.
 
 template <bool WIDE>
 struct TileShape {
@@ -693,18 +694,38 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
 
 template <int MODE>
 __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
-  const int nt = blockIdx.x;
-  const int mt = blockIdx.y;
+  const int gx = (int)gridDim.x;  // n-tiles; gridDim.y = m-tile slots (even)
+  int nt, mt, half;
+  if ((gx & 7) == 0) {
+    // Workgroups go to the 8 XCDs in turn by linear id L, and each XCD starts
+    // its own in increasing order: XCD c = L % 8 runs its s-th workgroup
+    // s = L / 8.  (c, s) maps to m-tile 2 (s / q) + c / 4 and n-tile
+    // (c % 4) q + s % q, q = gx / 4: XCD c takes every other m-tile and one
+    // quarter of the n-tiles, so each m-tile's activations are fetched by 4
+    // of the 8 L2s instead of all 8, and each weight n-tile by 2 instead of 1.
+    const int L = (int)blockIdx.x + gx * (int)blockIdx.y;
+    const int c = L & 7, s = L >> 3, q = gx >> 2;
+    const int mi = s / q, nn = s - mi * q;
+    mt = 2 * mi + (c >> 2);
+    nt = (c & 3) * q + nn;
+    // a half-empty m-tile pairs n-tiles inside the XCD's quarter
+    half = nn < (q >> 1) ? (q >> 1) : -(q >> 1);
+  } else {  // fewer than 8 n-tiles, or not a multiple of 8: the launch order
+    nt = (int)blockIdx.x;
+    mt = (int)blockIdx.y;
+    half = nt < (gx >> 1) ? (gx >> 1) : -(gx >> 1);
+  }
   // one load for the tile's expert, first pair row and row count
   const int4 ti = reinterpret_cast<const int4*>(a.tile_info)[mt];
   const int rows_here = ti.z;
   if (rows_here <= 0) return;  // past the last m-tile
   const int e = ti.x, row0 = 0, off = ti.y;
-  // a half-empty m-tile runs wide over n-tiles nt and nt + gx / 2 (gx = gridDim.x even)
-  const int half = (int)(gridDim.x >> 1);
-  const bool wide = rows_here <= 128 && (gridDim.x & 1) == 0;
+  // A half-empty m-tile runs wide over n-tile nt and its partner nt + half (the
+  // lower one of each pair works, the upper one exits).  The n-tile count (or
+  // the quarter q) is even whenever this applies.
+  const bool wide = rows_here <= 128 && (gx & 1) == 0;
   if (wide) {
-    if (nt >= half) return;
+    if (half < 0) return;
     tiled_tile<MODE, true>(a, nt, nt + half, e, row0, off, rows_here);
   } else {
     tiled_tile<MODE, false>(a, nt, nt, e, row0, off, rows_here);
@@ -756,7 +777,11 @@ __global__ void sq_reduce_kernel(const float* __restrict__ part, int64_t npairs,
 // ---------------------------------------------------------------------------
 // host side
 
-int64_t ffn_max_tiles(int64_t T, int64_t k, int64_t E) { return (T * k + Tiled::BM - 1) / Tiled::BM + E; }
+// m-tile slots: an upper bound on sum_e ceil(n_e / BM), rounded up to even (the XCD-aware tile order pairs them)
+int64_t ffn_max_tiles(int64_t T, int64_t k, int64_t E) {
+  const int64_t n = (T * k + Tiled::BM - 1) / Tiled::BM + E;
+  return n + (n & 1);
+}
 int ffn_sq_parts(int64_t H) { return (int)(H / 64); }  // small kernel: 64-column tiles (the finest split)
 bool ffn_use_small(int64_t T) { return T <= kSmallRows; }
 

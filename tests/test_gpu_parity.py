@@ -323,6 +323,9 @@ def test_layer_parity_config0(ops):
     ("stream_decode", 12, 2048, 2048, 8, 2),  # 8 iterations: two per wave in both stages
     ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: 12 iterations, three per wave (ends in the first buffer)
     ("decode_uneven_waves", 10, 1280, 384, 8, 2),  # gate_up: 5 iterations (2, 1, 1, 1); down: K 384, 128-k steps
+    # 8 n-tiles in both stages (I 1024, H 2048): the XCD-aware tile order, with full, ragged and wide m-tiles
+    ("xcd_tiles", 600, 2048, 1024, 5, 2),
+    ("xcd_tiles_wide", 250, 2048, 1024, 4, 2),
 ])
 def test_layer_parity_random(ops, name, T, H, I, E, k):
     case = random_case(name, zlib.crc32(name.encode()) % 1000, T, H, I, E, k)
