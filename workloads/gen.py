@@ -16,6 +16,8 @@ Recipe (per weight set, ``np.random.SeedSequence([0x4E5646, key, stream...])``):
   it stays BF16), then BF16 round-to-nearest-even;
 * rotation signs (the diagonal of the Hadamard rotation studied on the outlier
   layer): +-1 with equal probability, one draw per hidden size;
+* projection vectors (test data for the full-size output checks): N(0, 1)
+  float64 [H, n];
 * calibration batch: n_cal tokens of N(0, 1) -> BF16;
 * tokens of workload i: N(0, 1) -> BF16, drawn in chunks of 1024 rows, each
   chunk from its own stream so chunks can be drawn in parallel;
@@ -40,6 +42,7 @@ X_CHUNK = 1024
 # stream ids inside a weight set
 _S_ROUTER_W, _S_ROUTER_B, _S_XCAL, _S_SHARED, _S_EXPERT = 1, 2, 3, 4, 1000
 _ROTATION_KEY = 0x524F54
+_PROJECTION_KEY = 0x50524A
 
 
 def _rng(*keys: int) -> np.random.Generator:
@@ -79,6 +82,12 @@ def shared_expert_bf16(ws: WeightSet):
     """(W_gate [I,H], W_up [I,H], W_down [H,I]) BF16 bit patterns of the shared expert."""
     rng = _rng(ws.seed_key, _S_SHARED)
     return tuple(_weight(rng, shape, False) for shape in ((ws.I, ws.H), (ws.I, ws.H), (ws.H, ws.I)))
+
+
+def projection_vectors(H: int, n: int = 4) -> np.ndarray:
+    """n seeded N(0, 1) vectors of length H, float64 [H, n]: the directions on which the full-size checks
+    compare every token's layer output (test data, not part of the layer)."""
+    return _rng(_PROJECTION_KEY, H, n).standard_normal((H, n))
 
 
 def rotation_signs(n: int) -> np.ndarray:
