@@ -549,8 +549,11 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
   __shared__ int32_t off[257];
   const int e = threadIdx.x;
   int32_t s = 0;
-  if (e < E)
+  // unrolled so that the loads of several chunks are in flight together (integer sums: any order)
+  if (e < E) {
+#pragma unroll 16
     for (int c = 0; c < nchunks; ++c) s += chunk_counts[(int64_t)c * E + e];
+  }
   tot[e] = (e < E) ? s : 0;
   __syncthreads();
   if (e == 0) {
@@ -566,6 +569,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
     counts[e] = tot[e];
     offsets[e] = off[e];
     int32_t run = off[e];
+#pragma unroll 16
     for (int c = 0; c < nchunks; ++c) {
       chunk_base[(int64_t)c * E + e] = run;
       run += chunk_counts[(int64_t)c * E + e];
