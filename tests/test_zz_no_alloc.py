@@ -45,3 +45,37 @@ def test_noalloc_matches_workspace_call_on_shrinking_inputs(ops):
                                           r.expert_offsets, r.sorted_pair_ids, r.topk_w, po2, None)
         torch.cuda.synchronize()
         assert torch.equal(po2, po_ref), f"{name}: pair_out differs without pair_sqnorm"
+
+
+def test_noalloc_captured_in_a_graph(ops):
+    """The reason for the entry point: it can be captured in a HIP graph (no allocation, no memset
+    node).  One call is captured after an eager warm-up call, then the graph is replayed three
+    times, with eager work on the outputs and synchronizations between the replays.  Every replay
+    must equal the workspace call bitwise."""
+    case = random_case("noalloc_graph", 74, 200, 512, 256, 8, 2)
+    say(f"noalloc graph: T={case.T} H={case.H} I={case.I} E={case.E} k={case.k}")
+    layer = gpu_layer(case)
+    r, xc, xs = ops.moe_route_quantize(dev_bf16(case.x), layer.w_router, layer.bias, case.k, case.rsf, layer.x_gs)
+    n, H = case.T * case.k, case.H
+    po_ref = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    sq_ref = torch.empty((n,), dtype=torch.float32, device="cuda")
+    ops.moe_nvfp4_grouped_ffn(xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k, r.expert_offsets,
+                              r.sorted_pair_ids, r.topk_w, pair_out=po_ref, pair_sqnorm=sq_ref)
+    po = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    sq = torch.empty((n,), dtype=torch.float32, device="cuda")
+    args = (xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k, r.expert_offsets, r.sorted_pair_ids,
+            r.topk_w, po, sq)
+    ops.moe_nvfp4_grouped_ffn_noalloc(*args)  # eager: the per-device set-up happens outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.moe_nvfp4_grouped_ffn_noalloc(*args)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        po.fill_(float("nan"))
+        sq.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(po, po_ref), f"replay {rep}: pair_out differs"
+        assert torch.equal(sq, sq_ref), f"replay {rep}: pair_sqnorm differs"
