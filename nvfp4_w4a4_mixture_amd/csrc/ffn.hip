@@ -395,31 +395,42 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
   //
   // Ring: the prologue fills all NS slots.  At the mid-stage barrier of stage
   // st every wave has finished its reads of slot st % NS (lgkmcnt(0) before
-  // the barrier) and waited for its DMA of stage st + 1, so stage st + NS is
-  // issued into slot st % NS right after it.
+  // the barrier) and waited for its DMA of stage st + 1, so stage st + NS can
+  // go into slot st % NS from then on.  Its DMA is spread over the four
+  // sub-steps of the second half, a quarter each, between the MFMAs: issued
+  // in one block after the barrier, the DMA of all four waves queued in the
+  // address unit at once and held up every wave's MFMAs (gate_up 4.6% slower).
   const int64_t nst = K / 128;
   constexpr int L = S::kLoadsPerStage;
   static_assert((NS - 1) * L < 64, "vmcnt range");
   const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
-  auto issue_async = [&](int64_t st) {
+  // DMA ops lo .. hi - 1 of stage st, in the order A codes, A scales, B codes,
+  // B scales (L ops in all)
+  auto issue_ops = [&](int64_t st, auto lo_c, auto hi_c) {
+    constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
+    constexpr int o1 = S::kACodeOps, o2 = o1 + S::kAScaleOps, o3 = o2 + S::kBCodeOps;
     const uint32_t sb = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(st % NS) * (uint32_t)S::kStage);
     const uint8_t* ac = a.a_codes + st * 64;  // 128 k per stage
     const uint8_t* as = a.a_scales + st * 8;
     const uint8_t* bc = b_code_expert + st * 64;
     const uint8_t* bs = b_scale_expert + st * 128;
 #pragma unroll
-    for (int i = 0; i < S::kACodeOps; ++i) dma16_async(ac, a_code_off[i], sb + (4 * i + wave_u) * 1024u);
-#pragma unroll
-    for (int i = 0; i < S::kAScaleOps; ++i)
-      dma4_async(as, a_scale_off[i], sb + (uint32_t)S::kACodeBytes + (4 * i + wave_u) * 256u);
-#pragma unroll
-    for (int i = 0; i < S::kBCodeOps; ++i)
-      dma16_async(bc, b_code_off[i], sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (4 * i + wave_u) * 1024u);
-#pragma unroll
-    for (int i = 0; i < S::kBScaleOps; ++i)
-      dma4_async(bs, b_scale_off[i],
-                 sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (4 * i + wave_u) * 256u);
+    for (int o = lo; o < hi; ++o) {
+      if (o < o1) {
+        dma16_async(ac, a_code_off[o], sb + (4 * o + wave_u) * 1024u);
+      } else if (o < o2) {
+        dma4_async(as, a_scale_off[o - o1], sb + (uint32_t)S::kACodeBytes + (4 * (o - o1) + wave_u) * 256u);
+      } else if (o < o3) {
+        dma16_async(bc, b_code_off[o - o2],
+                    sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (4 * (o - o2) + wave_u) * 1024u);
+      } else {
+        dma4_async(bs, b_scale_off[o - o3],
+                   sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes + S::kBCodeBytes) + (4 * (o - o3) + wave_u) * 256u);
+      }
+    }
   };
+  using std::integral_constant;
+  auto issue_async = [&](int64_t st) { issue_ops(st, integral_constant<int, 0>{}, integral_constant<int, L>{}); };
   // this lane's fragment words of one half (fragment i of a row block sits
   // 2048 B = 32 rows after fragment i-1) and its scale words (256 B apart)
   auto load_half = [&](int64_t st, uint32_t slot, u32x4_t* fa, u32x4_t* fb) {
@@ -509,13 +520,18 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
       else if (ahead == 1) wait_vmcnt<L>();
       else wait_vmcnt<0>();
       barrier_after_lds();
-      if constexpr (kIssue) issue_async(st + NS);
       load_half(st + 1, slot_q0, n0a, n0b);
       load_scales(st + 1, nsa, nsb);
     }
 #pragma unroll
     for (int ss = 4; ss < 8; ++ss) {
       if (ss > 4) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kIssue) {
+        if (ss == 4) issue_ops(st + NS, integral_constant<int, 0>{}, integral_constant<int, L / 4>{});
+        else if (ss == 5) issue_ops(st + NS, integral_constant<int, L / 4>{}, integral_constant<int, L / 2>{});
+        else if (ss == 6) issue_ops(st + NS, integral_constant<int, L / 2>{}, integral_constant<int, 3 * L / 4>{});
+        else issue_ops(st + NS, integral_constant<int, 3 * L / 4>{}, integral_constant<int, L>{});
+      }
       if (ss < 7) {
         decode((ss + 1) & 1, c1a, c1b, (ss + 1) & 3, sa, sbv, 2 + (((ss + 1) & 3) >> 1));
       } else if (kMore) {
