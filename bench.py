@@ -33,6 +33,9 @@ if ROOT not in sys.path:
 
 METRIC = "routed-MoE layer tokens/sec (NVFP4 W4A4) + % HBM / % MFMA roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# Extra workloads: untimed busy time before timing (GPU clocks ramp up under load) and the shortest timed region
+EXTRA_BUSY_S = 0.2
+EXTRA_TIMED_S = 0.05
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 FFN_SOURCE = os.path.join(ROOT, "nvfp4_w4a4_mixture_amd", "csrc", "ffn.hip")
@@ -380,15 +383,38 @@ def _roof(bound: str, work: float, seconds: float) -> dict:
     return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": a / HBM_PEAK_GBS}
 
 
-def measure(cfg, layer, x, steps: int, warmup: int, reap: bool) -> dict:
+def _busy_steps(layer, x, reap: bool, seconds: float) -> tuple:
+    """Untimed steps until the GPU has run them for `seconds` of wall time (in chunks, each ended by a
+    device synchronization, so the host never queues far ahead).  Returns (steps run, seconds per step)."""
+    import torch
+
+    n, t0, chunk = 0, time.perf_counter(), 4
+    while True:
+        for _ in range(chunk):
+            layer(x, out_dtype=torch.bfloat16, reap=reap)
+        torch.cuda.synchronize()
+        n += chunk
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return n, dt / n
+        chunk = min(2 * chunk, 256)
+
+
+def measure(cfg, layer, x, steps: int, warmup: int, reap: bool, min_busy_s: float = 0.0,
+            min_timed_s: float = 0.0) -> dict:
     """Time `steps` whole-layer steps (after `warmup` untimed ones) on the current stream.
 
     The warm-up steps record HIP events around every stage (stage_ms_warmup) and pick the dominant FFN
     stage.  The timed region is `steps` steps with no events at all (each event recorded on the stream
     adds a gap), bracketed by device synchronizations: that wall time per step is the figure reported.
     A second pass of `steps` steps records events only around the dominant stage, for its kernel time.
-    Returns the wall time per step, the dominant kernel's mean event time and the routing counts of the
-    last step."""
+
+    min_busy_s > 0 adds untimed steps after the warm-up until the GPU has been busy for that long: its
+    clocks drop while it idles and take milliseconds of load to come back, longer than a few short
+    decode steps.  min_timed_s > 0 raises the number of timed steps so that the timed region lasts about
+    that long.  Both stay 0 for the headline, which runs exactly `warmup` and `steps` steps.
+    Returns the wall time per step, the steps and warm-up steps run, the dominant kernel's mean event
+    time and the routing counts of the last step."""
     import numpy as np
     import torch
 
@@ -401,6 +427,12 @@ def measure(cfg, layer, x, steps: int, warmup: int, reap: bool) -> dict:
     ms_stage = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in wev[skip:]])) for j, s in enumerate(stages)}
     dom = "gate_up" if ms_stage["gate_up"] >= ms_stage["down"] else "down"
     j_dom = stages.index(dom)
+    warm_run = max(warmup, 1)
+    if min_busy_s > 0:
+        n_busy, est = _busy_steps(layer, x, reap, min_busy_s)
+        warm_run += n_busy
+        if min_timed_s > 0:
+            steps = max(steps, int(np.ceil(min_timed_s / est)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -416,7 +448,8 @@ def measure(cfg, layer, x, steps: int, warmup: int, reap: bool) -> dict:
     torch.cuda.synchronize()
     dom_ms = float(np.mean([ev[j_dom].elapsed_time(ev[j_dom + 1]) for ev in events]))
     counts = out.route.expert_counts.cpu().numpy()
-    return dict(sec_per_step=sec, dom=dom, dom_ms=dom_ms, ms_stage=ms_stage, counts=counts)
+    return dict(sec_per_step=sec, dom=dom, dom_ms=dom_ms, ms_stage=ms_stage, counts=counts, steps=steps,
+                warmup=warm_run)
 
 
 def roofline_of(cfg, m: dict) -> dict:
@@ -493,13 +526,14 @@ def extra_workloads(main_cfg, main_layer, steps: int, warmup: int, flush_mib: in
         else:
             layer, _ = workload_io.build_layer(cfg, main_layer.device)
         x = workload_io.tokens(cfg, main_layer.device)
-        m = measure(cfg, layer, x, steps, warmup, reap=cfg.reap)
+        # each extra workload follows seconds of host-side set-up with the GPU idle: warm it up by busy time
+        m = measure(cfg, layer, x, steps, warmup, reap=cfg.reap, min_busy_s=EXTRA_BUSY_S, min_timed_s=EXTRA_TIMED_S)
         roof = roofline_of(cfg, m)
         rec = {"workload": f"{cfg.name}: {cfg.describe()}", "reap": cfg.reap, "tokens_per_s": cfg.T / m["sec_per_step"],
                "ms_per_step": m["sec_per_step"] * 1e3, "touched_experts": int((m["counts"] > 0).sum()),
-               "stage_ms_warmup": m["ms_stage"], "roofline": roof, "steps": steps, "warmup": warmup}
+               "stage_ms_warmup": m["ms_stage"], "roofline": roof, "steps": m["steps"], "warmup": m["warmup"]}
         if cfg.name == "decode":
-            rec["per_step_events"] = decode_cold_hot(cfg, layer, x, steps, warmup, flush_mib, cfg.reap)
+            rec["per_step_events"] = decode_cold_hot(cfg, layer, x, m["steps"], warmup, flush_mib, cfg.reap)
         out[cfg.name] = rec
         del layer, x
         torch.cuda.empty_cache()
