@@ -279,6 +279,10 @@ struct TileShape {
   static constexpr int kHStride = kHcols + 4;   // floats per LDS row of h
   static constexpr int kHBytes = kARows * kHStride * 4;
   static constexpr int kBody = NS * kStage > kHBytes ? NS * kStage : kHBytes;
+  // down epilogue: pair ids and weights, then the per-lane row sums of f^2 (4 waves x 32 lanes for wide tiles,
+  // 2 x 32 for full ones), rows padded to kARows + 4 floats
+  static constexpr int kSqLdsBytes = 2 * kARows * 4 + (WIDE ? 4 : 2) * 32 * (kARows + 4) * 4;
+  static_assert(kSqLdsBytes <= kBody, "down epilogue LDS");
   // DMA instructions per wave per stage: 16-byte code loads cover 16 rows,
   // 4-byte scale loads cover 32 rows
   static constexpr int kACodeOps = kARows / 64, kAScaleOps = kARows / 128;
@@ -287,9 +291,8 @@ struct TileShape {
 };
 struct Tiled {
   static constexpr int BM = 256, BN = 256, kHcols = 128;  // the full tile: m-tile height, n-tile width
-  static constexpr int kSqBytes = 2 * 2 * 128 * 4;          // down: Σf² partials [n-tile half][wn][row]
   static constexpr int kLds =
-      (TileShape<false>::kBody > TileShape<true>::kBody ? TileShape<false>::kBody : TileShape<true>::kBody) + kSqBytes;
+      TileShape<false>::kBody > TileShape<true>::kBody ? TileShape<false>::kBody : TileShape<true>::kBody;
 };
 static_assert(TileShape<false>::kHcols == Tiled::kHcols && TileShape<false>::kBRows == Tiled::BN &&
                   TileShape<false>::kARows == Tiled::BM, "full tile shape");
@@ -607,8 +610,6 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     // values derived from threadIdx.x at the top would be held across the loop.
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int r = lane_e & 31, g = lane_e >> 5;
-    // Σf² partials [n-tile half][wn][128 rows] (full tiles: [wn][256 rows])
-    float* sqbuf = reinterpret_cast<float*>(smem + (Tiled::kLds - Tiled::kSqBytes));
     // the tile's pair ids and weights, staged once in the (now free) ring
     int32_t* prow = reinterpret_cast<int32_t*>(smem);
     float* wrow = reinterpret_cast<float*>(smem + S::kARows * 4);
@@ -617,92 +618,72 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
       prow[t] = p;
       wrow[t] = t < rows_here ? a.topk_w[p] : 0.0f;
     }
+    // Each lane's sums of f^2 over its 4 columns, by row: sql[slot][r][row],
+    // slot = wn (full tiles; wm picks the rows) or the wave (wide tiles: wm is
+    // the n-tile), rows padded to a stride of kARows + 4 floats so that the
+    // 16-byte writes of 16 consecutive lanes cover all 64 banks.  After the
+    // barrier thread t adds up its row's partials in a fixed order.
+    constexpr int kSqStride = S::kARows + 4;
+    float* sql = reinterpret_cast<float*>(smem + 2 * S::kARows * 4);
+    float* sqw = sql + ((WIDE ? wave : wn) * 32 + r) * kSqStride;
     __syncthreads();
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
     const int64_t col0 = (int64_t)((WIDE && wm) ? nt2 : nt) * Tiled::BN + 128 * wn;  // this wave's first column
-    // Sum each row's f^2 over the 32 lanes of the half-wave with a transposed
-    // butterfly, two 32-row blocks (i = 2 ii, 2 ii + 1) at a time so that only
-    // 32 partials are live beside the accumulators: at each level a lane keeps
-    // half of its remaining rows and sends the other half to its partner
-    // (lane ^ mask), so the shuffles of a level are independent.  The masks go
-    // 1, 2, 8 (in-register DPP moves: 28 of the 31 shuffles of a pair) and then
-    // 4, 16 (LDS swizzles).  Lane r then holds the sum of row 16 il + q =
-    // 16 r0 + 8 r1 + 4 r3 + 2 r2 + r4 of the pair (r_b: bit b of r).  The order
-    // is fixed: deterministic.
-    auto xshfl = [](float x, int mask) -> float {
-      const int xi = __float_as_int(x);
-      int y;
-      if (mask == 1) y = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, false);        // quad_perm [1,0,3,2]
-      else if (mask == 2) y = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-      else if (mask == 8) y = __builtin_amdgcn_mov_dpp(xi, 0x128, 0xF, 0xF, false);  // row_ror:8 (16-lane rows)
-      else if (mask == 4) y = __builtin_amdgcn_ds_swizzle(xi, 0x101F);               // xor 4 within 32 lanes
-      else y = __builtin_amdgcn_ds_swizzle(xi, 0x401F);                              // xor 16 within 32 lanes
-      return __int_as_float(y);
-    };
-    // full tiles: sqbuf[wn][row]; wide tiles: sqbuf[wm][wn][row], wm = the n-tile
-    float* sqw = sqbuf + (WIDE ? wm * 256 + wn * 128 : wn * 256);
-    const int lrow = 16 * (r & 1) + 8 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1) + 2 * ((r >> 2) & 1) + (r >> 4);
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      // v[16 il + q]: this lane's sum of f^2 over its 4 columns of row (i = 2 ii + il, q)
-      float v[32];
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int il = 0; il < 2; ++il) {
-        const int i = 2 * ii + il;
+      for (int qh = 0; qh < 4; ++qh) {
+        // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
+        const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
+        const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
+        const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
+        float4 ss4;
 #pragma unroll
-        for (int qh = 0; qh < 4; ++qh) {
-          // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
-          const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
-          const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
-          const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
+        for (int qq = 0; qq < 4; ++qq) {
+          const int q = 4 * qh + qq, row = rb + qq;
+          const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
+          const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
+          // one bounds branch per row around its four stores (a branch per
+          // store made the compiler copy every accumulator out of the AGPRs
+          // ahead of the first one, and spill)
+          float* dst = a.pair_out + p * a.H + col0 + r;
+          float ss = 0.0f, fv[4];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int q = 4 * qh + qq, row = rb + qq;
-            const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
-            const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
-            // one bounds branch per row around its four stores (a branch per
-            // store made the compiler copy every accumulator out of the AGPRs
-            // ahead of the first one, and spill)
-            float* dst = a.pair_out + p * a.H + col0 + r;
-            float ss = 0.0f, fv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              fv[j] = acc[i][j][q] * alpha;
-              ss += fv[j] * fv[j];
-            }
-            if (row < rows_here) {
-              // written once and read once by the combine: non-temporal, so the
-              // weighted rows do not push the operand tiles out of L2
-#pragma unroll
-              for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(wp * fv[j], dst + 32 * j);
-            }
-            v[16 * il + q] = ss;
+          for (int j = 0; j < 4; ++j) {
+            fv[j] = acc[i][j][q] * alpha;
+            ss += fv[j] * fv[j];
           }
-        }
-      }
-      constexpr int kMask[5] = {1, 2, 8, 4, 16};
+          if (row < rows_here) {
+            // written once and read once by the combine: non-temporal, so the
+            // weighted rows do not push the operand tiles out of L2
 #pragma unroll
-      for (int lvl = 0; lvl < 5; ++lvl) {
-        const int mask = kMask[lvl], half = 16 >> lvl;
-        const bool up = (r & mask) != 0;
-#pragma unroll
-        for (int k = 0; k < half; ++k) {
-          const float send = up ? v[k] : v[k + half];
-          const float keep = up ? v[k + half] : v[k];
-          v[k] = keep + xshfl(send, mask);
+            for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(wp * fv[j], dst + 32 * j);
+          }
+          if (qq == 0) ss4.x = ss;
+          else if (qq == 1) ss4.y = ss;
+          else if (qq == 2) ss4.z = ss;
+          else ss4.w = ss;
         }
+        *reinterpret_cast<float4*>(sqw + rb) = ss4;
       }
-      const int i = 2 * ii + (lrow >> 4), q = lrow & 15;
-      sqw[a_row0 + 32 * i + 8 * (q >> 2) + 4 * g + (q & 3)] = v[0];
     }
     __syncthreads();
     if (a.sq_part != nullptr) {
+      // row t's sum: the 32 column lanes of each of its two waves in order, then the two waves
+      auto row_sum = [&](int slot0, int row) -> float {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll 8
+        for (int c = 0; c < 32; ++c) {
+          s0 += sql[(slot0 * 32 + c) * kSqStride + row];
+          s1 += sql[((slot0 + 1) * 32 + c) * kSqStride + row];
+        }
+        return s0 + s1;
+      };
       if (WIDE) {
         const int h = tid >> 7, row = tid & 127;  // 256 threads: 2 n-tiles x 128 rows
-        if (row < rows_here)
-          a.sq_part[(int64_t)prow[row] * a.n_part + (h ? nt2 : nt)] = sqbuf[h * 256 + row] + sqbuf[h * 256 + 128 + row];
+        if (row < rows_here) a.sq_part[(int64_t)prow[row] * a.n_part + (h ? nt2 : nt)] = row_sum(2 * h, row);
       } else if (tid < rows_here) {
-        a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = sqbuf[tid] + sqbuf[256 + tid];
+        a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = row_sum(0, tid);
       }
     }
   }
