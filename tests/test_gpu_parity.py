@@ -376,16 +376,29 @@ def test_zero_tokens_is_a_noop(ops):
     assert torch.all(out.saliency == 0)
 
 
-def test_repeat_runs_are_bitwise_identical(ops):
-    case = random_case("determinism", 9, 200, 256, 128, 8, 2)
-    say("determinism")
+@pytest.mark.parametrize("name,T,H,I,E,k", [
+    ("det_decode", 12, 512, 256, 16, 4),       # small-M kernels, single-workgroup permutation
+    ("det_tiled", 200, 256, 128, 8, 2),        # tiled kernels, ragged m-tiles
+    ("det_xcd_wide", 250, 2048, 1024, 4, 2),   # XCD-aware tile order with wide half-empty m-tiles
+])
+def test_repeat_runs_are_bitwise_identical(ops, name, T, H, I, E, k):
+    """Every reduction has a fixed order, so three runs of the same layer on the same input agree bit for bit in
+    every output: routing, codes, pair rows, norms, y and the saliency."""
+    case = random_case(name, 9, T, H, I, E, k)
+    say(f"determinism {name}")
     layer = gpu_layer(case)
     x = dev_bf16(case.x)
-    a = layer(x, out_dtype=torch.float32, reap=True)
-    ya, sa, pa = a.y.clone(), a.saliency.clone(), a.route.sorted_pair_ids.clone()
-    b = layer(x, out_dtype=torch.float32, reap=True)
-    torch.cuda.synchronize()
-    assert torch.equal(ya, b.y) and torch.equal(sa, b.saliency) and torch.equal(pa, b.route.sorted_pair_ids)
+
+    def snap(o):
+        return [o.y, o.saliency, o.route.topk_ids, o.route.topk_w, o.route.expert_offsets, o.route.sorted_pair_ids,
+                o.x_codes, o.x_scales, o.h_codes, o.h_scales, o.pair_out, o.pair_sqnorm]
+
+    first = [t.clone() for t in snap(layer(x, out_dtype=torch.float32, reap=True))]
+    for _ in range(2):
+        again = snap(layer(x, out_dtype=torch.float32, reap=True))
+        torch.cuda.synchronize()
+        for i, (u, v) in enumerate(zip(first, again)):
+            assert torch.equal(u, v), f"{name}: output {i} differs between runs"
 
 
 def test_prepack_roundtrip_and_canonical_weights(ops):
