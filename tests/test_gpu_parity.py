@@ -326,6 +326,11 @@ def test_layer_parity_config0(ops):
     # 8 n-tiles in both stages (I 1024, H 2048): the XCD-aware tile order, with full, ragged and wide m-tiles
     ("xcd_tiles", 600, 2048, 1024, 5, 2),
     ("xcd_tiles_wide", 250, 2048, 1024, 4, 2),
+    # k = 16: the combine sums each token's rows in two chunks of eight
+    ("k16_decode", 9, 256, 128, 32, 16),
+    ("k16_tiled", 150, 512, 256, 32, 16),
+    # 256 experts at decode size: the register/LDS logits kernel (more than 128 experts), 16 of 256 chosen
+    ("decode_e256_k16", 16, 256, 128, 256, 16),
 ])
 def test_layer_parity_random(ops, name, T, H, I, E, k):
     case = random_case(name, zlib.crc32(name.encode()) % 1000, T, H, I, E, k)
