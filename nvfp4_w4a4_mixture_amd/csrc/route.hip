@@ -259,9 +259,14 @@ constexpr int kMfmaChunk = 64;
 struct MfmaSplit {
   int64_t nsplit, hlen;
 };
-static MfmaSplit mfma_split(int64_t T, int64_t H) {
+// Batches: 16-token row blocks per wave.  Two blocks share each converted
+// router value between two MFMAs (half the BF16 -> FP64 converts per MFMA);
+// above 128 experts their accumulators would not fit, so one.
+static inline int mfma_row_blocks(int nt) { return nt <= 8 ? 2 : 1; }
+
+static MfmaSplit mfma_split(int64_t T, int64_t H, int nt) {
   if (T <= 16) return {(H + 255) / 256, 256};
-  const int64_t blocks = (T + 63) / 64;
+  const int64_t blocks = (T + 64 * mfma_row_blocks(nt) - 1) / (64 * mfma_row_blocks(nt));
   const int64_t nch = (H + kMfmaChunk - 1) / kMfmaChunk;
   int64_t ns = (kTargetWGs + blocks - 1) / blocks;
   ns = ns < 1 ? 1 : (ns > kMaxSplit ? kMaxSplit : ns);
@@ -278,7 +283,7 @@ __device__ __forceinline__ double bf16_pair_elem(const u32x4_t& lo, const u32x4_
 // QUANT: every lane also writes the NVFP4 quantization of its 16 x values (one
 // block) to codes [T, H/2] and scales [T, H/16] against the global scale *qgs
 // (the same steps as nvfp4_quantize_act); the grid covers each block once.
-template <int NT, bool SPLIT_H, bool QUANT>
+template <int NT, bool SPLIT_H, bool QUANT, int MB>
 __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* __restrict__ x, int64_t T, int64_t H,
                                                                 int64_t ldx, const uint16_t* __restrict__ wr, int E,
                                                                 int64_t hlen, double* __restrict__ part,
@@ -289,32 +294,43 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t split = blockIdx.y;
-  const int64_t t0 = SPLIT_H ? 0 : (int64_t)blockIdx.x * 64 + 16 * wave;
+  static_assert(!SPLIT_H || MB == 1, "decode: one row block");
+  // this wave's first token; its row blocks are t0 + 16 m, m < MB
+  const int64_t t0 = SPLIT_H ? 0 : (int64_t)blockIdx.x * (64 * MB) + 16 * MB * wave;
   const int64_t hs = split * hlen;
   const int64_t he = hs + hlen < H ? hs + hlen : H;
   const int64_t hb = SPLIT_H ? hs + kMfmaChunk * wave : hs;
   const int64_t hend = SPLIT_H ? (hb + kMfmaChunk < he ? hb + kMfmaChunk : he) : he;
-  // this lane's token row and expert rows (clamped; their results are not stored)
-  const int64_t t = t0 + r;
-  const uint16_t* xrow = x + (t < T ? t : T - 1) * ldx + 16 * g;
+  // this lane's token rows and expert rows (clamped; their results are not stored)
+  const uint16_t* xrow[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int64_t t = t0 + 16 * m + r;
+    xrow[m] = x + (t < T ? t : T - 1) * ldx + 16 * g;
+  }
   const uint16_t* wrow[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const int e = 16 * n + r;
     wrow[n] = wr + (int64_t)(e < E ? e : E - 1) * H + 16 * g;
   }
-  double4_t acc[NT];
+  double4_t acc[MB][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = double4_t{0.0, 0.0, 0.0, 0.0};
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[m][n] = double4_t{0.0, 0.0, 0.0, 0.0};
   struct Chunk {
-    u32x4_t a[2];
+    u32x4_t a[MB][2];
     u32x4_t b[NT][2];
   };
   auto load = [&](int64_t h0, Chunk& d) {
     const bool in = h0 + 16 * g < hend;  // H % 16 == 0: a lane group's 16 h are all in or all out
     const u32x4_t z = {0u, 0u, 0u, 0u};
-    d.a[0] = in ? *reinterpret_cast<const u32x4_t*>(xrow + h0) : z;
-    d.a[1] = in ? *reinterpret_cast<const u32x4_t*>(xrow + h0 + 8) : z;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      d.a[m][0] = in ? *reinterpret_cast<const u32x4_t*>(xrow[m] + h0) : z;
+      d.a[m][1] = in ? *reinterpret_cast<const u32x4_t*>(xrow[m] + h0 + 8) : z;
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       d.b[n][0] = in ? *reinterpret_cast<const u32x4_t*>(wrow[n] + h0) : z;
@@ -323,28 +339,37 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
   };
   const float gsq = QUANT ? qgs[0] : 0.0f;
   auto quantize = [&](int64_t h0, const Chunk& d) {
-    if (t < T && h0 + 16 * g < hend) {
-      float f[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t w = d.a[i >> 2][i & 3];
-        f[2 * i] = bf16_to_f32(w & 0xFFFFu);
-        f[2 * i + 1] = bf16_to_f32(w >> 16);
+    for (int m = 0; m < MB; ++m) {
+      const int64_t t = t0 + 16 * m + r;
+      if (t < T && h0 + 16 * g < hend) {
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w = d.a[m][i >> 2][i & 3];
+          f[2 * i] = bf16_to_f32(w & 0xFFFFu);
+          f[2 * i + 1] = bf16_to_f32(w >> 16);
+        }
+        uint32_t lo, hi;
+        const uint32_t sc = quantize_block16(f, gsq, lo, hi);
+        const int64_t hblk = h0 + 16 * g;
+        *reinterpret_cast<uint2*>(qcodes + t * (H / 2) + hblk / 2) = make_uint2(lo, hi);
+        qscales[t * (H / 16) + hblk / 16] = (uint8_t)sc;
       }
-      uint32_t lo, hi;
-      const uint32_t sc = quantize_block16(f, gsq, lo, hi);
-      const int64_t hblk = h0 + 16 * g;
-      *reinterpret_cast<uint2*>(qcodes + t * (H / 2) + hblk / 2) = make_uint2(lo, hi);
-      qscales[t * (H / 16) + hblk / 16] = (uint8_t)sc;
     }
   };
   auto compute = [&](const Chunk& d) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const double av = bf16_pair_elem(d.a[0], d.a[1], s);
+      double av[MB];
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-        acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bf16_pair_elem(d.b[n][0], d.b[n][1], s), acc[n], 0, 0, 0);
+      for (int m = 0; m < MB; ++m) av[m] = bf16_pair_elem(d.a[m][0], d.a[m][1], s);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const double bv = bf16_pair_elem(d.b[n][0], d.b[n][1], s);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[m], bv, acc[m][n], 0, 0, 0);
+      }
     }
   };
   if (hb < hend) {
@@ -362,7 +387,7 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave - 1][n][lane][i] = acc[n][i];
+        for (int i = 0; i < 4; ++i) red[wave - 1][n][lane][i] = acc[0][n][i];
     }
     __syncthreads();
     if (wave != 0) return;
@@ -370,30 +395,34 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[n][i] = ((acc[n][i] + red[0][n][lane][i]) + red[1][n][lane][i]) + red[2][n][lane][i];
+        acc[0][n][i] = ((acc[0][n][i] + red[0][n][lane][i]) + red[1][n][lane][i]) + red[2][n][lane][i];
   }
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int e = 16 * n + r;
+  for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t tt = t0 + g + 4 * i;
-      if (tt < T && e < E) part[(split * T + tt) * E + e] = acc[n][i];
+    for (int n = 0; n < NT; ++n) {
+      const int e = 16 * n + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t tt = t0 + 16 * m + g + 4 * i;
+        if (tt < T && e < E) part[(split * T + tt) * E + e] = acc[m][n][i];
+      }
     }
-  }
 }
 
 template <int NT, bool SPLIT_H>
 static void launch_logits_mfma(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, const uint16_t* wr, int E,
                                MfmaSplit sp, double* part, const float* qgs, uint8_t* qcodes, uint8_t* qscales,
                                hipStream_t st) {
-  const dim3 grid(SPLIT_H ? 1u : (unsigned)((T + 63) / 64), (unsigned)sp.nsplit);
+  constexpr int MB = SPLIT_H ? 1 : (NT <= 8 ? 2 : 1);
+  static_assert(SPLIT_H || MB == (NT <= 8 ? 2 : 1), "row blocks as mfma_row_blocks");
+  const dim3 grid(SPLIT_H ? 1u : (unsigned)((T + 64 * MB - 1) / (64 * MB)), (unsigned)sp.nsplit);
   if (qcodes)
-    hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H, true>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E,
+    hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H, true, MB>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E,
                        sp.hlen, part, qgs, qcodes, qscales);
   else
-    hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H, false>), grid, dim3(256), 0, st, x, T, H, ldx, wr, E,
-                       sp.hlen, part, qgs, qcodes, qscales);
+    hipLaunchKernelGGL((route_logits_mfma_kernel<NT, SPLIT_H, false, MB>), grid, dim3(256), 0, st, x, T, H, ldx, wr,
+                       E, sp.hlen, part, qgs, qcodes, qscales);
 }
 
 // Smallest instantiated n-tile count covering E experts (E <= 256).
@@ -628,7 +657,7 @@ size_t route_workspace_bytes(int64_t T, int64_t H, int64_t E, int64_t k) {
   const RouteSplit sp = route_split(T, H);
   int64_t nsplit = sp.nsplit;
   if (T <= kDecT && dec_nsplit(H) > nsplit) nsplit = dec_nsplit(H);
-  if (mfma_split(T, H).nsplit > nsplit) nsplit = mfma_split(T, H).nsplit;
+  if (mfma_split(T, H, mfma_nt((int)E)).nsplit > nsplit) nsplit = mfma_split(T, H, mfma_nt((int)E)).nsplit;
   return align256((size_t)(2 * nchunks * E * 4)) + (size_t)(nsplit * T * E * 8);
 }
 
@@ -659,7 +688,7 @@ hipError_t launch_route(const uint16_t* x, int64_t T, int64_t H, int64_t ldx, co
   const bool mfma = vec16 && H % 16 == 0 && (T > kDecT || nt <= 8);
   int64_t nsplit = 0;
   if (mfma) {
-    const MfmaSplit ms = mfma_split(T, H);
+    const MfmaSplit ms = mfma_split(T, H, nt);
     nsplit = ms.nsplit;
     const bool split_h = T <= kDecT;
 #define LM(N)                                                                  \
