@@ -256,16 +256,22 @@ void ffn_small_kernel(FfnArgs a) {
 // m-tile with at most 128 rows is run wide instead: 128 pair rows x 512 weight
 // rows (n-tile nt and a partner n-tile, waves 1 x 4 over the weight rows), and
 // the workgroups of the partner n-tiles exit, so no MFMA work goes to the
-// empty half.  Workgroups go to the 8 XCDs in turn by linear id; the partner
+// empty half; one of at most 64 rows runs as a half tile, 64 x 512, with half
+// the MFMA work.  Workgroups go to the 8 XCDs in turn by linear id; the partner
 // is chosen so that the working workgroups stay spread over all XCDs: with the
 // XCD-aware tile order (a multiple of 8 n-tiles) it is the n-tile half a
 // quarter away inside the same XCD's quarter, otherwise nt + gx / 2.
 
-template <bool WIDE>
+// SHAPE 0: full tile, 256 pair rows x 256 weight rows (waves 2 x 2 of 128 x 128);
+// 1: wide, 128 x 512 (waves 1 x 4 of 128 x 128); 2: half, 64 x 512 (waves
+// 1 x 4 of 64 x 128, half the MFMA work of the others).
+template <int SHAPE>
 struct TileShape {
-  static constexpr int kARows = WIDE ? 128 : 256;  // pair rows (A)
-  static constexpr int kBRows = WIDE ? 512 : 256;  // weight rows (B)
-  static constexpr int NS = WIDE ? 3 : 4;          // ring stages of 128 k
+  static constexpr bool kWide = SHAPE != 0;                             // two n-tiles
+  static constexpr int kARows = SHAPE == 0 ? 256 : SHAPE == 1 ? 128 : 64;  // pair rows (A)
+  static constexpr int kBRows = SHAPE == 0 ? 256 : 512;                 // weight rows (B)
+  static constexpr int NA = (SHAPE == 0 ? kARows / 2 : kARows) / 32;   // A fragments per wave: 4, 4, 2
+  static constexpr int NS = SHAPE == 0 ? 4 : 3;                         // ring stages of 128 k
   // codes: [row][4 slots of 16 B], chunk c of row r in slot c ^ ((r >> 2) & 3):
   // 16 lanes reading one chunk of 16 consecutive rows, and the 16 lanes of a
   // DMA group writing the 4 chunks of 4 consecutive rows, each touch 16
@@ -281,30 +287,34 @@ struct TileShape {
   static constexpr int kBody = NS * kStage > kHBytes ? NS * kStage : kHBytes;
   // down epilogue: pair ids and weights, then the per-lane row sums of f^2 (4 waves x 32 lanes for wide tiles,
   // 2 x 32 for full ones), rows padded to kARows + 4 floats
-  static constexpr int kSqLdsBytes = 2 * kARows * 4 + (WIDE ? 4 : 2) * 32 * (kARows + 4) * 4;
+  static constexpr int kSqLdsBytes = 2 * kARows * 4 + (kWide ? 4 : 2) * 32 * (kARows + 4) * 4;
   static_assert(kSqLdsBytes <= kBody, "down epilogue LDS");
   // DMA instructions per wave per stage: 16-byte code loads cover 16 rows,
-  // 4-byte scale loads cover 32 rows
-  static constexpr int kACodeOps = kARows / 64, kAScaleOps = kARows / 128;
+  // 4-byte scale loads cover 32 rows.  The half tile's 64 rows of A scales
+  // are two such loads; waves w and w + 2 both issue the one for rows
+  // 32 (w % 2) .., writing the same bytes, so every wave issues as many
+  // loads as the others.
+  static constexpr int kACodeOps = kARows / 64, kAScaleOps = kARows >= 128 ? kARows / 128 : 1;
   static constexpr int kBCodeOps = kBRows / 64, kBScaleOps = kBRows / 128;
   static constexpr int kLoadsPerStage = kACodeOps + kAScaleOps + kBCodeOps + kBScaleOps;
 };
+constexpr int max3(int x, int y, int z) { return x > y ? (x > z ? x : z) : (y > z ? y : z); }
 struct Tiled {
   static constexpr int BM = 256, BN = 256, kHcols = 128;  // the full tile: m-tile height, n-tile width
-  static constexpr int kLds =
-      TileShape<false>::kBody > TileShape<true>::kBody ? TileShape<false>::kBody : TileShape<true>::kBody;
+  static constexpr int kLds = max3(TileShape<0>::kBody, TileShape<1>::kBody, TileShape<2>::kBody);
 };
-static_assert(TileShape<false>::kHcols == Tiled::kHcols && TileShape<false>::kBRows == Tiled::BN &&
-                  TileShape<false>::kARows == Tiled::BM, "full tile shape");
+static_assert(TileShape<0>::kHcols == Tiled::kHcols && TileShape<0>::kBRows == Tiled::BN &&
+                  TileShape<0>::kARows == Tiled::BM, "full tile shape");
 static_assert(Tiled::kLds <= 160 * 1024, "LDS");
 
 // One tile: expert e's pair rows off + row0 .. off + row0 + rows_here - 1
 // (rows of the expert-sorted pair order) against n-tile nt (and nt2 when WIDE).
-template <int MODE, bool WIDE>
+template <int MODE, int SHAPE>
 __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, int e, int row0, int off,
                                            int rows_here) {
-  using S = TileShape<WIDE>;
-  constexpr int NS = S::NS;
+  using S = TileShape<SHAPE>;
+  constexpr bool WIDE = S::kWide;
+  constexpr int NS = S::NS, NA = S::NA;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: kept in scalar registers
@@ -356,11 +366,16 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     b_code_off[i] = (uint32_t)((b_row(row) - erow0) * kbytes) + 16 * chunk;
   }
-  // 4-byte scale DMA i of this wave: rows 32 q .. 32 q + 31, q = 4 i + wave; lane -> row 32 q + lane / 2, dword lane % 2
+  // 4-byte scale DMA i of this wave: rows 32 q .. 32 q + 31, q = 4 i + wave (A of the half tile: q = wave % 2);
+  // lane -> row 32 q + lane / 2, dword lane % 2
+  auto a_scale_block = [&](int i) -> int {  // the 32-row block of A-scale DMA i
+    if constexpr (S::kARows >= 128) return 4 * i + wave;
+    else return (4 * i + wave) % (S::kARows / 32);
+  };
   uint32_t a_scale_off[S::kAScaleOps], b_scale_off[S::kBScaleOps];
 #pragma unroll
   for (int i = 0; i < S::kAScaleOps; ++i) {
-    const int row = 32 * (4 * i + wave) + (lane >> 1);
+    const int row = 32 * a_scale_block(i) + (lane >> 1);
     a_scale_off[i] = (uint32_t)(a_row(row) * kscales) + 4 * (lane & 1);
   }
 #pragma unroll
@@ -369,9 +384,9 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     b_scale_off[i] = (uint32_t)tiled_scale_index(br, 0, K) + 4 * (lane & 1);  // tiled: 128 B per stage
   }
 
-  float16_t acc[4][4];
+  float16_t acc[NA][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -422,7 +437,8 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
       if (o < o1) {
         dma16_async(ac, a_code_off[o], sb + (4 * o + wave_u) * 1024u);
       } else if (o < o2) {
-        dma4_async(as, a_scale_off[o - o1], sb + (uint32_t)S::kACodeBytes + (4 * (o - o1) + wave_u) * 256u);
+        const uint32_t blk = S::kARows >= 128 ? 4u * (uint32_t)(o - o1) + wave_u : wave_u % (uint32_t)(S::kARows / 32);
+        dma4_async(as, a_scale_off[o - o1], sb + (uint32_t)S::kACodeBytes + blk * 256u);
       } else if (o < o3) {
         dma16_async(bc, b_code_off[o - o2],
                     sb + (uint32_t)(S::kACodeBytes + S::kAScaleBytes) + (4 * (o - o2) + wave_u) * 1024u);
@@ -439,7 +455,7 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
   auto load_half = [&](int64_t st, uint32_t slot, u32x4_t* fa, u32x4_t* fb) {
     const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NA; ++i)
       fa[i] = *reinterpret_cast<const u32x4_t*>(smem + sb + a_lane + 16u * slot + 2048u * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -448,33 +464,35 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
   auto load_scales = [&](int64_t st, uint32_t* sa, uint32_t* sbv) {
     const uint32_t sb = (uint32_t)(st % NS) * (uint32_t)S::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(smem + sb + as_lane + 256u * i);
+    for (int i = 0; i < NA; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(smem + sb + as_lane + 256u * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) sbv[j] = *reinterpret_cast<const uint32_t*>(smem + sb + bs_lane + 256u * j);
   };
   // sub-step ss (q = ss / 4 half, dword ss % 4) uses scale byte 2 q + (ss % 4) / 2 of the lane's word
-  half8_t da[2][4], db[2][4];
+  half8_t da[2][NA], db[2][4];
   auto decode = [&](int buf, const u32x4_t* fa, const u32x4_t* fb, int w, const uint32_t* sa, const uint32_t* sbv,
                     int sbyte) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) da[buf][i] = decode8(fa[i][w], scale_pair(sa[i], sbyte));
+    for (int i = 0; i < NA; ++i) da[buf][i] = decode8(fa[i][w], scale_pair(sa[i], sbyte));
 #pragma unroll
     for (int j = 0; j < 4; ++j) db[buf][j] = decode8(fb[j][w], scale_pair(sbv[j], sbyte));
   };
   // the 16 MFMAs of a sub-step, each followed by a slice of the next
   // sub-step's decode and, for the first n_ds, by one of the LDS reads just
   // issued in program order (so they go out early instead of just before use)
+  // (the half tile: 8 MFMAs per sub-step beside 6 decoded fragments, so 7 VALU slots each)
+  constexpr int kValuSlots = NA == 4 ? 6 : 7;
   auto mfma16 = [&](int buf, int n_ds) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[buf][i], db[buf][j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < 4 * NA; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (m < n_ds) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuSlots, 0);  // VALU
     }
   };
 
@@ -490,8 +508,8 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     else wait_vmcnt<0>();
   }
   barrier_after_lds();
-  u32x4_t c0a[4], c0b[4];
-  uint32_t sa[4], sbv[4];
+  u32x4_t c0a[NA], c0b[4];
+  uint32_t sa[NA], sbv[4];
   load_half(0, slot_q0, c0a, c0b);
   load_scales(0, sa, sbv);
   decode(0, c0a, c0b, 0, sa, sbv, 0);
@@ -503,7 +521,7 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     // Each sub-step is its own scheduling region (sched_barrier), so no
     // decode, and no scale convert in particular, is hoisted next to the
     // LDS read it depends on; the reads are issued at the top of a half.
-    u32x4_t c1a[4], c1b[4];
+    u32x4_t c1a[NA], c1b[4];
     __builtin_amdgcn_sched_barrier(0);
     load_half(st, slot_q1, c1a, c1b);
 #pragma unroll
@@ -511,10 +529,10 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
       if (ss > 0) __builtin_amdgcn_sched_barrier(0);
       if (ss < 3) decode((ss + 1) & 1, c0a, c0b, ss + 1, sa, sbv, (ss + 1) >> 1);
       else decode(0, c1a, c1b, 0, sa, sbv, 2);
-      mfma16(ss & 1, ss == 0 ? 8 : 0);
+      mfma16(ss & 1, ss == 0 ? (NA + 4 < 8 ? NA + 4 : 8) : 0);
     }
-    u32x4_t n0a[4], n0b[4];
-    uint32_t nsa[4], nsb[4];
+    u32x4_t n0a[NA], n0b[4];
+    uint32_t nsa[NA], nsb[4];
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kMore) {
       // stage st + 1 has landed; the stages issued after it (up to NS - 2) may stay in flight
@@ -543,8 +561,10 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
         // the wave would wait for the LDS there.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          asm volatile("" : "+v"(nsa[i]), "+v"(nsb[i]));
-          asm volatile("" : "+v"(n0a[i]), "+v"(n0b[i]));
+          if (i < NA) asm volatile("" : "+v"(nsa[i]));
+          asm volatile("" : "+v"(nsb[i]));
+          if (i < NA) asm volatile("" : "+v"(n0a[i]));
+          asm volatile("" : "+v"(n0b[i]));
         }
         decode(0, n0a, n0b, 0, nsa, nsb, 0);
       }
@@ -553,9 +573,9 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     if constexpr (kMore) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c0a[i] = n0a[i];
+        if (i < NA) c0a[i] = n0a[i];
         c0b[i] = n0b[i];
-        sa[i] = nsa[i];
+        if (i < NA) sa[i] = nsa[i];
         sbv[i] = nsb[i];
       }
     }
@@ -574,7 +594,7 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     const float alpha_g = 1.0f / (a.a_gs[0] * a.b_gs[2 * e]);
     const float alpha_u = 1.0f / (a.a_gs[0] * a.b_gs[2 * e + 1]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -630,7 +650,7 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
     const int64_t col0 = (int64_t)((WIDE && wm) ? nt2 : nt) * Tiled::BN + 128 * wn;  // this wave's first column
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NA; ++i) {
 #pragma unroll
       for (int qh = 0; qh < 4; ++qh) {
         // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
@@ -680,8 +700,8 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
         return s0 + s1;
       };
       if (WIDE) {
-        const int h = tid >> 7, row = tid & 127;  // 256 threads: 2 n-tiles x 128 rows
-        if (row < rows_here) a.sq_part[(int64_t)prow[row] * a.n_part + (h ? nt2 : nt)] = row_sum(2 * h, row);
+        const int h = tid / S::kARows, row = tid % S::kARows;  // 2 n-tiles x kARows rows (of 256 threads)
+        if (h < 2 && row < rows_here) a.sq_part[(int64_t)prow[row] * a.n_part + (h ? nt2 : nt)] = row_sum(2 * h, row);
       } else if (tid < rows_here) {
         a.sq_part[(int64_t)prow[tid] * a.n_part + nt] = row_sum(0, tid);
       }
@@ -718,14 +738,16 @@ __global__ __launch_bounds__(256) void ffn_tiled_kernel(FfnArgs a) {
   if (rows_here <= 0) return;  // past the last m-tile
   const int e = ti.x, row0 = 0, off = ti.y;
   // A half-empty m-tile runs wide over n-tile nt and its partner nt + half (the
-  // lower one of each pair works, the upper one exits).  The n-tile count (or
-  // the quarter q) is even whenever this applies.
+  // lower one of each pair works, the upper one exits), as 128 rows or, with
+  // at most 64 rows, as the half tile.  The n-tile count (or the quarter q) is
+  // even whenever this applies.
   const bool wide = rows_here <= 128 && (gx & 1) == 0;
   if (wide) {
     if (half < 0) return;
-    tiled_tile<MODE, true>(a, nt, nt + half, e, row0, off, rows_here);
+    if (rows_here <= 64) tiled_tile<MODE, 2>(a, nt, nt + half, e, row0, off, rows_here);
+    else tiled_tile<MODE, 1>(a, nt, nt + half, e, row0, off, rows_here);
   } else {
-    tiled_tile<MODE, false>(a, nt, nt, e, row0, off, rows_here);
+    tiled_tile<MODE, 0>(a, nt, nt, e, row0, off, rows_here);
   }
 }
 

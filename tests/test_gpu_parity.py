@@ -319,6 +319,12 @@ def test_layer_parity_config0(ops):
     ("e1_rows128_wide", 128, 512, 256, 1, 1),
     ("e1_rows129_full", 129, 512, 256, 1, 1),
     ("e1_rows384_full_then_wide", 384, 512, 256, 1, 1),
+    # a last m-tile of <= 64 rows runs as the half tile (64 rows x two n-tiles); 65 rows stays wide
+    ("e1_rows64_half", 64, 512, 256, 1, 1),
+    ("e1_rows17_half", 17, 512, 256, 1, 1),
+    ("e1_rows65_wide", 65, 512, 256, 1, 1),
+    ("e1_rows320_full_then_half", 320, 512, 256, 1, 1),
+    ("many_small_half", 60, 512, 256, 32, 4),
     # decode kernel (T <= 16): four waves take 256-k iterations in turn through two register buffers
     ("stream_decode", 12, 2048, 2048, 8, 2),  # 8 iterations: two per wave in both stages
     ("stream_three_steps", 5, 3072, 2048, 6, 3),  # gate_up: 12 iterations, three per wave (ends in the first buffer)
@@ -326,6 +332,7 @@ def test_layer_parity_config0(ops):
     # 8 n-tiles in both stages (I 1024, H 2048): the XCD-aware tile order, with full, ragged and wide m-tiles
     ("xcd_tiles", 600, 2048, 1024, 5, 2),
     ("xcd_tiles_wide", 250, 2048, 1024, 4, 2),
+    ("xcd_tiles_half", 120, 2048, 1024, 5, 2),
     # k = 16: the combine sums each token's rows in two chunks of eight
     ("k16_decode", 9, 256, 128, 32, 16),
     ("k16_tiled", 150, 512, 256, 32, 16),
