@@ -104,7 +104,8 @@ def stage_bytes_flops(cfg, counts):
     w13 = 2 * I * H * nv
     w2 = H * I * nv
     gate_up_bytes = touched * w13 + T * H * nv + pairs * I * nv  # weights + x codes + h codes out
-    down_bytes = touched * w2 + pairs * I * nv + pairs * H * 4  # weights + h codes + pair_out (fp32)
+    # weights + h codes + pair rows (FP16 values and one FP32 scale per row)
+    down_bytes = touched * w2 + pairs * I * nv + pairs * (H * 2 + 4)
     return dict(touched=touched,
                 gate_up=dict(bytes=gate_up_bytes, flops=2.0 * pairs * H * 2 * I, per_expert_bytes=w13),
                 down=dict(bytes=down_bytes, flops=2.0 * pairs * I * H, per_expert_bytes=w2))
@@ -262,7 +263,7 @@ def shared_study(cfg, layer, x, steps: int, warmup: int) -> dict:
     def serial():
         ops.moe_shared_expert(x, w13, w2, out=out, workspace=ws)
         o = layer(x, out_dtype=torch.bfloat16, reap=False)
-        ops.moe_combine_block(o.pair_out, out, T, cfg.k, torch.bfloat16, y=o.y)
+        ops.moe_combine_block(o.pair_out, o.pair_scale, out, T, cfg.k, torch.bfloat16, y=o.y)
 
     ms_routed = step_ms(lambda: layer(x, out_dtype=torch.bfloat16, reap=False))
     ms_block = step_ms(lambda: layer(x, out_dtype=torch.bfloat16, reap=False, block=True))

@@ -47,6 +47,18 @@
  *                 (r / 16) * K + (b / 8) * 128 + (r % 16) * 8 + b % 8,
  *             i.e. an array [R/16, K/128, 16, 8].  A K-step of an expert
  *             kernel then reads its 16 rows' scales as one contiguous run.
+ *  Pair rows  The weighted expert output of pair p, w_p * f, as FP16 values
+ *             pair_out [T*k, H] (IEEE binary16 bits) times a power of two
+ *             pair_scale [T*k] (FP32): value = fp16(pair_out[p, c]) *
+ *             pair_scale[p], which is exact in FP32.  pair_scale[p] = 2^E with
+ *             E = floor(log2(B)) - 14, clamped to [-126, 113], for the bound
+ *             B = |w_p| * (I * 2688^2) * (1 / (h_gs[e] * w2_gs[e])) (FP32
+ *             operations in that order) that no FP4 operands can exceed
+ *             (2688 = 6 * 448, the largest decoded element); every stored
+ *             value is then below 2^15 in magnitude, and pair_out[p, c] =
+ *             fp16_rne(f32(w_p * 2^-E) * f[c]).  For values above 2^-29 * B
+ *             (FP16's normal range) that rounding is within 2^-11 relative,
+ *             well below the BF16 rounding of the output.
  *  Errors     Arguments are validated on the host before anything is
  *             enqueued.  A failed check returns its status, enqueues nothing
  *             and writes no output.  T == 0 (rows == 0) is a successful no-op
@@ -181,8 +193,8 @@ moe_status moe_nvfp4_unpack_weights(const uint8_t* packed_codes, const uint8_t* 
  *         the decoded values, FP32 accumulation)
  *     h = silu(g) * u in FP32, quantized to NVFP4 with h_gs[e]
  *     f = hhat . W_down[e]^T                          (same arithmetic)
- *     pair_out[p, :] = topk_w[p] * f                  (FP32, [T*k, H])
- *     pair_sqnorm[p] = sum_h f[h]^2 (unweighted f; only if pair_sqnorm != NULL)
+ *     pair row p = topk_w[p] * f     (pair_out and pair_scale, see "Pair rows")
+ *     pair_sqnorm[p] = sum_h f[h]^2 (unweighted FP32 f; only if pair_sqnorm != NULL)
  *
  * x_codes [T, H/2], x_scales [T, H/16] (from nvfp4_quantize_act), x_gs
  * device FP32 [1]; weights in the layout of the header comment; h_gs [E]
@@ -195,7 +207,7 @@ moe_status moe_nvfp4_unpack_weights(const uint8_t* packed_codes, const uint8_t* 
  * 256-byte aligned; it holds the re-quantized h, the tile schedule and the
  * per-tile partial sums of f^2.
  * Code arrays, activation scale arrays (x_scales, h_scales) and pair_out
- * must be 16-byte aligned, weight scale arrays 4-byte aligned.
+ * must be 16-byte aligned, weight scale arrays and pair_scale 4-byte aligned.
  * Pairs not listed in sorted_pair_ids are not written. */
 size_t moe_ffn_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I);
 moe_status moe_nvfp4_grouped_ffn(
@@ -204,7 +216,7 @@ moe_status moe_nvfp4_grouped_ffn(
     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
     const float* h_gs, int64_t E, int64_t I, int64_t k,
     const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
-    float* pair_out, float* pair_sqnorm,
+    uint16_t* pair_out, float* pair_scale, float* pair_sqnorm,
     void* workspace, size_t workspace_bytes, void* stream);
 
 /* The two stages of moe_nvfp4_grouped_ffn as separate calls, with the
@@ -223,7 +235,8 @@ moe_status moe_nvfp4_down_scatter(
     const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs, int64_t T, int64_t H,
     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int64_t E, int64_t I,
     int64_t k, const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
-    float* pair_out, float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream);
+    uint16_t* pair_out, float* pair_scale, float* pair_sqnorm, void* workspace, size_t workspace_bytes,
+    void* stream);
 
 /* moe_nvfp4_grouped_ffn for callers that cannot allocate device memory or
  * pass a workspace (code under HIP graph capture, tight serving loops,
@@ -242,16 +255,18 @@ moe_status moe_nvfp4_grouped_ffn_noalloc(
     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
     const float* h_gs, int64_t E, int64_t I, int64_t k,
     const int32_t* expert_offsets, const int32_t* sorted_pair_ids, const float* topk_w,
-    float* pair_out, float* pair_sqnorm, void* stream);
+    uint16_t* pair_out, float* pair_scale, float* pair_sqnorm, void* stream);
 
 /* ------------------------------------------------------------------------ */
-/* Weighted combine: y[t, :] = sum_{j=0..k-1} pair_out[t*k + j, :], summed in
- * j order (deterministic).  pair_out already carries the routing weight
+/* Weighted combine: y[t, :] = sum_{j=0..k-1} pair row t*k + j (see "Pair
+ * rows": fp16(pair_out) * pair_scale, exact in FP32), summed in FP32 in j
+ * order (deterministic).  The pair rows already carry the routing weight
  * ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card, "Pruning Setup":
  * renormalized sigmoid routing weights).  out_dtype 0 writes BF16
- * (round-to-nearest-even), 1 writes FP32.  H % 4 == 0; 16-byte aligned. */
-moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype,
-                       void* y, void* stream);
+ * (round-to-nearest-even), 1 writes FP32.  H % 8 == 0; pair_out and y 16-byte,
+ * pair_scale 4-byte aligned. */
+moe_status moe_combine(const uint16_t* pair_out, const float* pair_scale, int64_t T, int64_t k, int64_t H,
+                       int32_t out_dtype, void* y, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* REAP saliency ("K-EXAONE-152B-A23B-REAP-80E-BF16" model card, "Pruning
@@ -265,10 +280,10 @@ moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w,
                          int64_t T, int64_t k, int64_t E, float* saliency, void* stream);
 
 /* moe_combine and reap_saliency in one launch (the same results): y from
- * pair_out as moe_combine writes it, and saliency [E] as reap_saliency writes
- * it.  Same arguments and requirements as the two calls. */
-moe_status moe_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype,
-                            void* y, const float* pair_sqnorm, const float* topk_w,
+ * the pair rows as moe_combine writes it, and saliency [E] as reap_saliency
+ * writes it.  Same arguments and requirements as the two calls. */
+moe_status moe_combine_reap(const uint16_t* pair_out, const float* pair_scale, int64_t T, int64_t k, int64_t H,
+                            int32_t out_dtype, void* y, const float* pair_sqnorm, const float* topk_w,
                             const int32_t* expert_offsets, const int32_t* sorted_pair_ids, int64_t E,
                             float* saliency, void* stream);
 
@@ -312,7 +327,7 @@ moe_status moe_gather_experts(const void* src, int64_t E_src, int64_t bytes_per_
  *   g = x . W_gate^T, u = x . W_up^T      (BF16 products, FP32 accumulation)
  *   h = bf16_rne(silu(g) * u)             (the input of the BF16 down Linear)
  *   shared_out = h . W_down^T             (FP32, [T, H])
- *   block y[t] = sum_j pair_out[t*k + j] + shared_out[t]
+ *   block y[t] = sum_j pair row t*k + j + shared_out[t]
  *
  * x [T, H] BF16 with row stride ldx (ldx >= H, ldx % 8 == 0); w13 [2I, H]
  * BF16, gate rows 0..I-1 then up rows I..2I-1; w2 [H, I] BF16; h [T, I] BF16.
@@ -334,10 +349,10 @@ moe_status moe_shared_down(const uint16_t* h_bf16, int64_t T, int64_t I, const u
                            int64_t H, float* shared_out, void* workspace, size_t workspace_bytes,
                            void* stream);
 /* moe_combine with the shared expert's row added after the k routed rows:
- * y[t] = (sum_j pair_out[t*k + j]) + shared_out[t], FP32, then written as in
+ * y[t] = (sum_j pair row t*k + j) + shared_out[t], FP32, then written as in
  * moe_combine.  shared_out [T, H] FP32, 16-byte aligned. */
-moe_status moe_combine_block(const float* pair_out, const float* shared_out, int64_t T, int64_t k,
-                             int64_t H, int32_t out_dtype, void* y, void* stream);
+moe_status moe_combine_block(const uint16_t* pair_out, const float* pair_scale, const float* shared_out,
+                             int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Offline Hadamard rotation of the hidden dimension ("[NetsPresso AQ Deep

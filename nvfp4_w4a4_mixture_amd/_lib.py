@@ -40,23 +40,23 @@ SIGNATURES = {
     "moe_ffn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "moe_ffn_stage_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "moe_nvfp4_grouped_ffn": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
-                                     _p, _p, _p, _p, _p, _p, _sz, _p]),
+                                     _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "moe_nvfp4_grouped_ffn_noalloc": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64,
-                                             _p, _p, _p, _p, _p, _p]),
+                                             _p, _p, _p, _p, _p, _p, _p]),
     "moe_nvfp4_gate_up_swiglu": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p,
                                         _p, _p, _p, _sz, _p]),
     "moe_nvfp4_down_scatter": (_i32, [_p, _p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p,
-                                      _p, _p, _sz, _p]),
-    "moe_combine": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p]),
+                                      _p, _p, _p, _sz, _p]),
+    "moe_combine": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "reap_saliency": (_i32, [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p]),
-    "moe_combine_reap": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i64, _p, _p]),
+    "moe_combine_reap": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p, _p, _p, _p, _i64, _p, _p]),
     "reap_prune_select": (_i32, [_p, _i64, _i64, _p, _p]),
     "moe_gather_experts": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p]),
     "moe_shared_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "moe_shared_expert": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _sz, _p]),
     "moe_shared_gate_up": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
     "moe_shared_down": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p, _sz, _p]),
-    "moe_combine_block": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p]),
+    "moe_combine_block": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p]),
     "hadamard_rotate_bf16": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p]),
     "moe_nvfp4_prepack_weights": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p, _p]),
     "moe_nvfp4_unpack_weights": (_i32, [_p, _p, _i64, _i64, _i64, _i32, _p, _p, _p]),

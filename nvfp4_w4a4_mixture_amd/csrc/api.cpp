@@ -243,8 +243,8 @@ static moe_status gate_up_impl(const uint8_t* x_codes, const uint8_t* x_scales, 
 static moe_status down_impl(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs, int64_t T, int64_t H,
                             const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs, int64_t E,
                             int64_t I, int64_t k, const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
-                            const float* topk_w, float* pair_out, float* pair_sqnorm, unsigned char* ws,
-                            bool build_schedule, hipStream_t st) {
+                            const float* topk_w, uint16_t* pair_out, float* pair_scale, float* pair_sqnorm,
+                            unsigned char* ws, bool build_schedule, hipStream_t st) {
   const FfnWs L = ffn_ws_layout(T, k, E, H, I);
   moe::FfnArgs a{};
   a.a_codes = h_codes;
@@ -262,6 +262,7 @@ static moe_status down_impl(const uint8_t* h_codes, const uint8_t* h_scales, con
   a.topk_w = topk_w;
   a.tile_info = reinterpret_cast<const int32_t*>(ws + L.tile_info);
   a.pair_out = pair_out;
+  a.pair_scale = pair_scale;
   a.sq_part = pair_sqnorm ? reinterpret_cast<float*>(ws + L.sq_part) : nullptr;
   a.n_part = moe::ffn_use_small(T) ? (int)(H / 64) : (int)(H / moe::ffn_tiled_bn());
   if (moe_status s = launched(moe::launch_ffn_stage(1, a, T, E, build_schedule, st), "moe_nvfp4_down_scatter"))
@@ -297,24 +298,24 @@ moe_status moe_nvfp4_gate_up_swiglu(const uint8_t* x_codes, const uint8_t* x_sca
 moe_status moe_nvfp4_down_scatter(const uint8_t* h_codes, const uint8_t* h_scales, const float* h_gs, int64_t T,
                                   int64_t H, const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
                                   int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
-                                  const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
-                                  float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
+                                  const int32_t* sorted_pair_ids, const float* topk_w, uint16_t* pair_out,
+                                  float* pair_scale, float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
   if (moe_status s = check_ffn_shapes(T, H, E, I, k)) return s;
   if (T == 0) return MOE_OK;  // zero-size arrays may be NULL
   if (!h_codes || !h_scales || !h_gs || !w2_codes || !w2_scales || !w2_gs || !expert_offsets || !sorted_pair_ids ||
-      !topk_w || !pair_out)
+      !topk_w || !pair_out || !pair_scale)
     return fail(MOE_ERR_NULL, "moe_nvfp4_down_scatter: a required pointer is NULL");
   if (!aligned(h_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) || !aligned(h_scales, 16) ||
-      !aligned(w2_scales, 4))
-    return fail(MOE_ERR_ALIGN,
-                "moe_nvfp4_down_scatter: code arrays, h_scales and pair_out must be 16-byte, weight scales 4-byte aligned");
+      !aligned(w2_scales, 4) || !aligned(pair_scale, 4))
+    return fail(MOE_ERR_ALIGN, "moe_nvfp4_down_scatter: code arrays, h_scales and pair_out must be 16-byte, weight "
+                               "scales and pair_scale 4-byte aligned");
   const size_t need = ffn_ws_layout(T, k, E, H, I).total_stage;
   if (!workspace || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "moe_nvfp4_down_scatter: workspace needs %zu bytes", need);
   if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (moe_status s = check_device()) return s;
   return down_impl(h_codes, h_scales, h_gs, T, H, w2_codes, w2_scales, w2_gs, E, I, k, expert_offsets,
-                   sorted_pair_ids, topk_w, pair_out, pair_sqnorm, static_cast<unsigned char*>(workspace),
+                   sorted_pair_ids, topk_w, pair_out, pair_scale, pair_sqnorm, static_cast<unsigned char*>(workspace),
                    /*build_schedule=*/true, (hipStream_t)stream);
 }
 
@@ -324,15 +325,16 @@ static moe_status check_grouped_ffn(const char* fn, const uint8_t* x_codes, cons
                                     const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
                                     const float* w2_gs, const float* h_gs, int64_t E, int64_t I, int64_t k,
                                     const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
-                                    const float* topk_w, const float* pair_out) {
+                                    const float* topk_w, const uint16_t* pair_out, const float* pair_scale) {
   if (moe_status s = check_ffn_shapes(T, H, E, I, k)) return s;
   if (T == 0) return MOE_OK;  // zero-size arrays may be NULL
   if (!x_codes || !x_scales || !x_gs || !w13_codes || !w13_scales || !w13_gs || !w2_codes || !w2_scales || !w2_gs ||
-      !h_gs || !expert_offsets || !sorted_pair_ids || !topk_w || !pair_out)
+      !h_gs || !expert_offsets || !sorted_pair_ids || !topk_w || !pair_out || !pair_scale)
     return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (!aligned(x_codes, 16) || !aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(pair_out, 16) ||
-      !aligned(x_scales, 16) || !aligned(w13_scales, 4) || !aligned(w2_scales, 4))
-    return fail(MOE_ERR_ALIGN, "%s: code arrays, x_scales and pair_out must be 16-byte, weight scales 4-byte aligned",
+      !aligned(x_scales, 16) || !aligned(w13_scales, 4) || !aligned(w2_scales, 4) || !aligned(pair_scale, 4))
+    return fail(MOE_ERR_ALIGN,
+                "%s: code arrays, x_scales and pair_out must be 16-byte, weight scales and pair_scale 4-byte aligned",
                 fn);
   return MOE_OK;
 }
@@ -342,8 +344,8 @@ static moe_status grouped_ffn_impl(const uint8_t* x_codes, const uint8_t* x_scal
                                    int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
                                    const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
                                    const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
-                                   const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
-                                   float* pair_sqnorm, unsigned char* ws, hipStream_t st) {
+                                   const int32_t* sorted_pair_ids, const float* topk_w, uint16_t* pair_out,
+                                   float* pair_scale, float* pair_sqnorm, unsigned char* ws, hipStream_t st) {
   const FfnWs L = ffn_ws_layout(T, k, E, H, I);
   uint8_t* h_codes = ws + L.h_codes;
   uint8_t* h_scales = ws + L.h_scales;
@@ -352,19 +354,20 @@ static moe_status grouped_ffn_impl(const uint8_t* x_codes, const uint8_t* x_scal
     return s;
   // stage 2 reuses the schedule stage 1 built in the same workspace
   return down_impl(h_codes, h_scales, h_gs, T, H, w2_codes, w2_scales, w2_gs, E, I, k, expert_offsets,
-                   sorted_pair_ids, topk_w, pair_out, pair_sqnorm, ws, /*build_schedule=*/false, st);
+                   sorted_pair_ids, topk_w, pair_out, pair_scale, pair_sqnorm, ws, /*build_schedule=*/false, st);
 }
 
 moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales, const float* x_gs, int64_t T,
                                  int64_t H, const uint8_t* w13_codes, const uint8_t* w13_scales, const float* w13_gs,
                                  const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gs,
                                  const float* h_gs, int64_t E, int64_t I, int64_t k, const int32_t* expert_offsets,
-                                 const int32_t* sorted_pair_ids, const float* topk_w, float* pair_out,
-                                 float* pair_sqnorm, void* workspace, size_t workspace_bytes, void* stream) {
+                                 const int32_t* sorted_pair_ids, const float* topk_w, uint16_t* pair_out,
+                                 float* pair_scale, float* pair_sqnorm, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   const char* fn = "moe_nvfp4_grouped_ffn";
   if (moe_status s = check_grouped_ffn(fn, x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes,
                                        w2_scales, w2_gs, h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w,
-                                       pair_out))
+                                       pair_out, pair_scale))
     return s;
   if (T == 0) return MOE_OK;
   const FfnWs L = ffn_ws_layout(T, k, E, H, I);
@@ -373,7 +376,7 @@ moe_status moe_nvfp4_grouped_ffn(const uint8_t* x_codes, const uint8_t* x_scales
   if (!aligned(workspace, 256)) return fail(MOE_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (moe_status s = check_device()) return s;
   return grouped_ffn_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs,
-                          h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_sqnorm,
+                          h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_scale, pair_sqnorm,
                           static_cast<unsigned char*>(workspace), (hipStream_t)stream);
 }
 
@@ -418,11 +421,12 @@ moe_status moe_nvfp4_grouped_ffn_noalloc(const uint8_t* x_codes, const uint8_t* 
                                          const float* w13_gs, const uint8_t* w2_codes, const uint8_t* w2_scales,
                                          const float* w2_gs, const float* h_gs, int64_t E, int64_t I, int64_t k,
                                          const int32_t* expert_offsets, const int32_t* sorted_pair_ids,
-                                         const float* topk_w, float* pair_out, float* pair_sqnorm, void* stream) {
+                                         const float* topk_w, uint16_t* pair_out, float* pair_scale,
+                                         float* pair_sqnorm, void* stream) {
   const char* fn = "moe_nvfp4_grouped_ffn_noalloc";
   if (moe_status s = check_grouped_ffn(fn, x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes,
                                        w2_scales, w2_gs, h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w,
-                                       pair_out))
+                                       pair_out, pair_scale))
     return s;
   if (T == 0) return MOE_OK;
   const FfnWs L = ffn_ws_layout(T, k, E, H, I);
@@ -435,19 +439,21 @@ moe_status moe_nvfp4_grouped_ffn_noalloc(const uint8_t* x_codes, const uint8_t* 
   // nothing in the workspace needs to start at zero: the schedule is rebuilt and
   // every h row and partial sum is written before it is read
   return grouped_ffn_impl(x_codes, x_scales, x_gs, T, H, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs,
-                          h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_sqnorm,
+                          h_gs, E, I, k, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_scale, pair_sqnorm,
                           static_cast<unsigned char*>(ws), (hipStream_t)stream);
 }
 
-moe_status moe_combine(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y,
-                       void* stream) {
-  if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))
-    return fail(MOE_ERR_SHAPE, "moe_combine: need T >= 0, k >= 1, H a positive multiple of 4, out_dtype 0 or 1");
+moe_status moe_combine(const uint16_t* pair_out, const float* pair_scale, int64_t T, int64_t k, int64_t H,
+                       int32_t out_dtype, void* y, void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || H % 8 != 0 || (out_dtype != 0 && out_dtype != 1))
+    return fail(MOE_ERR_SHAPE, "moe_combine: need T >= 0, k >= 1, H a positive multiple of 8, out_dtype 0 or 1");
   if (T == 0) return MOE_OK;
-  if (!pair_out || !y) return fail(MOE_ERR_NULL, "moe_combine: a required pointer is NULL");
-  if (!aligned(pair_out, 16) || !aligned(y, 16)) return fail(MOE_ERR_ALIGN, "moe_combine: 16-byte alignment required");
+  if (!pair_out || !pair_scale || !y) return fail(MOE_ERR_NULL, "moe_combine: a required pointer is NULL");
+  if (!aligned(pair_out, 16) || !aligned(y, 16) || !aligned(pair_scale, 4))
+    return fail(MOE_ERR_ALIGN, "moe_combine: pair_out and y must be 16-byte, pair_scale 4-byte aligned");
   if (moe_status s = check_device()) return s;
-  return launched(moe::launch_combine(pair_out, nullptr, T, k, H, out_dtype, y, (hipStream_t)stream), "moe_combine");
+  return launched(moe::launch_combine(pair_out, pair_scale, nullptr, T, k, H, out_dtype, y, (hipStream_t)stream),
+                  "moe_combine");
 }
 
 moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w, const int32_t* expert_offsets,
@@ -463,19 +469,21 @@ moe_status reap_saliency(const float* pair_sqnorm, const float* topk_w, const in
                   "reap_saliency");
 }
 
-moe_status moe_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int32_t out_dtype, void* y,
-                            const float* pair_sqnorm, const float* topk_w, const int32_t* expert_offsets,
+moe_status moe_combine_reap(const uint16_t* pair_out, const float* pair_scale, int64_t T, int64_t k, int64_t H,
+                            int32_t out_dtype, void* y, const float* pair_sqnorm, const float* topk_w, const int32_t* expert_offsets,
                             const int32_t* sorted_pair_ids, int64_t E, float* saliency, void* stream) {
   const char* fn = "moe_combine_reap";
-  if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))
-    return fail(MOE_ERR_SHAPE, "%s: need T >= 0, k >= 1, H a positive multiple of 4, out_dtype 0 or 1", fn);
+  if (T < 0 || k < 1 || H <= 0 || H % 8 != 0 || (out_dtype != 0 && out_dtype != 1))
+    return fail(MOE_ERR_SHAPE, "%s: need T >= 0, k >= 1, H a positive multiple of 8, out_dtype 0 or 1", fn);
   if (E < 1 || E > 256 || T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "%s: need 1 <= E <= 256", fn);
-  if (!expert_offsets || !saliency || (T > 0 && (!pair_out || !y || !pair_sqnorm || !topk_w || !sorted_pair_ids)))
+  if (!expert_offsets || !saliency ||
+      (T > 0 && (!pair_out || !pair_scale || !y || !pair_sqnorm || !topk_w || !sorted_pair_ids)))
     return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
-  if (T > 0 && (!aligned(pair_out, 16) || !aligned(y, 16))) return fail(MOE_ERR_ALIGN, "%s: 16-byte alignment required", fn);
+  if (T > 0 && (!aligned(pair_out, 16) || !aligned(y, 16) || !aligned(pair_scale, 4)))
+    return fail(MOE_ERR_ALIGN, "%s: pair_out and y must be 16-byte, pair_scale 4-byte aligned", fn);
   if (moe_status s = check_device()) return s;
-  return launched(moe::launch_combine_reap(pair_out, T, k, H, out_dtype, y, pair_sqnorm, topk_w, expert_offsets,
-                                           sorted_pair_ids, E, saliency, (hipStream_t)stream),
+  return launched(moe::launch_combine_reap(pair_out, pair_scale, T, k, H, out_dtype, y, pair_sqnorm, topk_w,
+                                           expert_offsets, sorted_pair_ids, E, saliency, (hipStream_t)stream),
                   fn);
 }
 
@@ -593,16 +601,17 @@ moe_status moe_shared_expert(const uint16_t* x_bf16, int64_t T, int64_t H, int64
   return moe_shared_down(h, T, I, w2_bf16, H, shared_out, rest, workspace_bytes - hbytes, stream);
 }
 
-moe_status moe_combine_block(const float* pair_out, const float* shared_out, int64_t T, int64_t k, int64_t H,
-                             int32_t out_dtype, void* y, void* stream) {
-  if (T < 0 || k < 1 || H <= 0 || H % 4 != 0 || (out_dtype != 0 && out_dtype != 1))
-    return fail(MOE_ERR_SHAPE, "moe_combine_block: need T >= 0, k >= 1, H a positive multiple of 4, out_dtype 0 or 1");
+moe_status moe_combine_block(const uint16_t* pair_out, const float* pair_scale, const float* shared_out, int64_t T,
+                             int64_t k, int64_t H, int32_t out_dtype, void* y, void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || H % 8 != 0 || (out_dtype != 0 && out_dtype != 1))
+    return fail(MOE_ERR_SHAPE, "moe_combine_block: need T >= 0, k >= 1, H a positive multiple of 8, out_dtype 0 or 1");
   if (T == 0) return MOE_OK;
-  if (!pair_out || !shared_out || !y) return fail(MOE_ERR_NULL, "moe_combine_block: a required pointer is NULL");
-  if (!aligned(pair_out, 16) || !aligned(shared_out, 16) || !aligned(y, 16))
-    return fail(MOE_ERR_ALIGN, "moe_combine_block: 16-byte alignment required");
+  if (!pair_out || !pair_scale || !shared_out || !y)
+    return fail(MOE_ERR_NULL, "moe_combine_block: a required pointer is NULL");
+  if (!aligned(pair_out, 16) || !aligned(shared_out, 16) || !aligned(y, 16) || !aligned(pair_scale, 4))
+    return fail(MOE_ERR_ALIGN, "moe_combine_block: pair_out, shared_out and y must be 16-byte, pair_scale 4-byte aligned");
   if (moe_status s = check_device()) return s;
-  return launched(moe::launch_combine(pair_out, shared_out, T, k, H, out_dtype, y, (hipStream_t)stream),
+  return launched(moe::launch_combine(pair_out, pair_scale, shared_out, T, k, H, out_dtype, y, (hipStream_t)stream),
                   "moe_combine_block");
 }
 

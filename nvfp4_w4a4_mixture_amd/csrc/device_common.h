@@ -16,6 +16,7 @@
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -126,6 +127,26 @@ __device__ __forceinline__ half2_t scale_pair(uint32_t scales4, int k) {
 __device__ __forceinline__ float silu(float g) {
   const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
   return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Pair rows are stored as FP16 values times a power of two 2^E per row, with E
+// from a bound on |w_p f| that no operands can exceed: a decoded element
+// (code times E4M3 scale) is at most 6 * 448 = 2688 in magnitude, so an FP32
+// accumulator over K products is at most K * 2688^2 (to within its rounding)
+// and |w_p f| <= |w_p| * K * 2688^2 * alpha.  E = floor(log2(bound)) - 14
+// keeps every stored value below 2^15, inside FP16's finite range (largest
+// 65504).  A loose bound costs no precision: FP16 keeps 11 significant bits
+// over its normal range, which reaches 29 binades below 2^15.  E is clamped to
+// [-126, 113], so that 2^E and 2^-E are normal floats; a finite bound never
+// reaches the upper end, and below the lower one the values are too small to
+// reach 2^15.  Returns 2^-E, the factor applied before the FP16 rounding, and
+// sets scale = 2^E, the row's scale.
+__device__ __forceinline__ float pair_row_scale(float wp, int64_t K, float alpha, float& scale) {
+  const float bound = fabsf(wp) * ((float)K * 7225344.0f) * alpha;  // 2688^2 = 7225344
+  const int eb = (int)((__float_as_uint(bound) >> 23) & 255u) - 127;  // floor(log2(bound)) when bound is normal
+  const int E = min(max(eb - 14, -126), 113);
+  scale = __uint_as_float((uint32_t)(127 + E) << 23);
+  return __uint_as_float((uint32_t)(127 - E) << 23);
 }
 
 // Weight block scales are stored tiled: the 16 x 8 scale bytes of 16

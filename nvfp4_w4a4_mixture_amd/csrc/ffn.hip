@@ -4,7 +4,8 @@
 //
 //   stage 1 (gate_up): g, u = xhat . W_gate^T, xhat . W_up^T ; h = silu(g) * u,
 //                       h re-quantized to NVFP4 with the expert's calibrated gs_h
-//   stage 2 (down):    f = hhat . W_down^T ; pair_out[p] = w_p * f ; sum f^2
+//   stage 2 (down):    f = hhat . W_down^T ; pair_out[p] = w_p * f (FP16 times a
+//                       power-of-two scale per pair row) ; sum f^2
 //
 // Both operands stay FP4 in memory.  Each lane decodes its MFMA operand in
 // registers: 8 E2M1 codes (one dword) -> 8 FP16 values times the E4M3 block
@@ -241,8 +242,14 @@ void ffn_small_kernel(FfnArgs a) {
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 16);
     if (erow < Me) {
-      float4 out = make_float4(ep_w * f[0], ep_w * f[1], ep_w * f[2], ep_w * f[3]);
-      *reinterpret_cast<float4*>(a.pair_out + ep_pair * a.H + (int64_t)tile * 64 + 4 * q) = out;
+      float sc;
+      const float m = ep_w * pair_row_scale(ep_w, a.K, alpha, sc);  // w_p 2^-E, exact
+      half4_t out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = (_Float16)(m * f[i]);
+      *reinterpret_cast<half4_t*>(reinterpret_cast<_Float16*>(a.pair_out) + ep_pair * a.H + (int64_t)tile * 64 + 4 * q) =
+          out;
+      if (tile == 0 && q == 0) a.pair_scale[ep_pair] = sc;
       if (a.sq_part != nullptr && q == 0) a.sq_part[ep_pair * a.n_part + tile] = ss;
     }
   }
@@ -630,13 +637,22 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     // values derived from threadIdx.x at the top would be held across the loop.
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int r = lane_e & 31, g = lane_e >> 5;
-    // the tile's pair ids and weights, staged once in the (now free) ring
+    // the tile's pair ids and weights w_p 2^-E (E: the row's scale exponent), staged once in the (now free)
+    // ring; the workgroup of n-tile 0 writes the rows' scales 2^E
+    const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
     int32_t* prow = reinterpret_cast<int32_t*>(smem);
     float* wrow = reinterpret_cast<float*>(smem + S::kARows * 4);
     for (int t = tid; t < S::kARows; t += 256) {
       const int32_t p = t < rows_here ? a.sorted[off + row0 + t] : 0;
       prow[t] = p;
-      wrow[t] = t < rows_here ? a.topk_w[p] : 0.0f;
+      float m = 0.0f;
+      if (t < rows_here) {
+        const float wp = a.topk_w[p];
+        float sc;
+        m = wp * pair_row_scale(wp, a.K, alpha, sc);
+        if (nt == 0) a.pair_scale[p] = sc;
+      }
+      wrow[t] = m;
     }
     // Each lane's sums of f^2 over its 4 columns, by row: sql[slot][r][row],
     // slot = wn (full tiles; wm picks the rows) or the wave (wide tiles: wm is
@@ -647,13 +663,12 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
     float* sql = reinterpret_cast<float*>(smem + 2 * S::kARows * 4);
     float* sqw = sql + ((WIDE ? wave : wn) * 32 + r) * kSqStride;
     __syncthreads();
-    const float alpha = 1.0f / (a.a_gs[e] * a.b_gs[e]);
     const int64_t col0 = (int64_t)((WIDE && wm) ? nt2 : nt) * Tiled::BN + 128 * wn;  // this wave's first column
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
 #pragma unroll
       for (int qh = 0; qh < 4; ++qh) {
-        // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and weights in one read each
+        // rows rb .. rb + 3 (q = 4 qh .. 4 qh + 3): their pair ids and scaled weights in one read each
         const int rb = a_row0 + 32 * i + 8 * qh + 4 * g;
         const int4 p4 = *reinterpret_cast<const int4*>(prow + rb);
         const float4 w4 = *reinterpret_cast<const float4*>(wrow + rb);
@@ -662,11 +677,11 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
         for (int qq = 0; qq < 4; ++qq) {
           const int q = 4 * qh + qq, row = rb + qq;
           const int64_t p = qq == 0 ? p4.x : qq == 1 ? p4.y : qq == 2 ? p4.z : p4.w;
-          const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;
+          const float wp = qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w;  // w_p 2^-E
           // one bounds branch per row around its four stores (a branch per
           // store made the compiler copy every accumulator out of the AGPRs
           // ahead of the first one, and spill)
-          float* dst = a.pair_out + p * a.H + col0 + r;
+          _Float16* dst = reinterpret_cast<_Float16*>(a.pair_out) + p * a.H + col0 + r;
           float ss = 0.0f, fv[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -677,7 +692,7 @@ __device__ __forceinline__ void tiled_tile(const FfnArgs& a, int nt, int nt2, in
             // written once and read once by the combine: non-temporal, so the
             // weighted rows do not push the operand tiles out of L2
 #pragma unroll
-            for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(wp * fv[j], dst + 32 * j);
+            for (int j = 0; j < 4; ++j) __builtin_nontemporal_store((_Float16)(wp * fv[j]), dst + 32 * j);
           }
           if (qq == 0) ss4.x = ss;
           else if (qq == 1) ss4.y = ss;

@@ -49,7 +49,8 @@ struct FfnArgs {
   const int32_t* tile_info;
   uint8_t* h_codes;  // gate_up output
   uint8_t* h_scales;
-  float* pair_out;  // down outputs
+  uint16_t* pair_out;  // down outputs: FP16 [T*k, H], value = pair_out * pair_scale[row]
+  float* pair_scale;   // [T*k] powers of two
   float* sq_part;   // [T*k, n_part] partial sums of f^2, or null
   int n_part;
 };
@@ -80,12 +81,12 @@ int ffn_tiled_bn();
 hipError_t launch_ffn_stage(int mode, FfnArgs a, int64_t T, int64_t E, bool build_schedule, hipStream_t st);
 hipError_t launch_sq_reduce(const float* part, int64_t npairs, int n_part, float* out, hipStream_t st);
 
-// y = sum_j pair_out[t*k + j] (+ add[t] if add != null)
-hipError_t launch_combine(const float* pair_out, const float* add, int64_t T, int64_t k, int64_t H, int out_dtype,
-                          void* y, hipStream_t st);
+// y = sum_j pair_out[t*k + j] * pair_scale[t*k + j] (+ add[t] if add != null)
+hipError_t launch_combine(const uint16_t* pair_out, const float* pair_scale, const float* add, int64_t T, int64_t k,
+                          int64_t H, int out_dtype, void* y, hipStream_t st);
 hipError_t launch_reap(const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                        int64_t E, float* saliency, hipStream_t st);
-hipError_t launch_combine_reap(const float* pair_out, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
+hipError_t launch_combine_reap(const uint16_t* pair_out, const float* pair_scale, int64_t T, int64_t k, int64_t H, int out_dtype, void* y,
                                const float* sq, const float* topk_w, const int32_t* offsets, const int32_t* sorted,
                                int64_t E, float* saliency, hipStream_t st);
 hipError_t launch_prune_select(const float* saliency, int64_t E, int64_t n_keep, int32_t* keep_ids, hipStream_t st);

@@ -24,7 +24,8 @@ class LayerOut:
     route: ops.RouteOut
     x_codes: torch.Tensor
     x_scales: torch.Tensor
-    pair_out: torch.Tensor
+    pair_out: torch.Tensor  # FP16 [T*k, H]: pair row p = pair_out[p] * pair_scale[p]
+    pair_scale: torch.Tensor  # FP32 [T*k], powers of two
     pair_sqnorm: Optional[torch.Tensor]
     saliency: Optional[torch.Tensor]
     shared_out: Optional[torch.Tensor] = None  # the shared expert's FP32 output (block=True)
@@ -81,7 +82,8 @@ class NVFP4MoELayer:
                 route_ws=torch.empty((max(ops.moe_route_workspace_bytes(T, H, E, k), 1),), dtype=torch.uint8, device=d),
                 x_codes=torch.empty((T, H // 2), dtype=torch.uint8, device=d),
                 x_scales=torch.empty((T, H // 16), dtype=torch.uint8, device=d),
-                pair_out=torch.empty((T * k, H), dtype=torch.float32, device=d),
+                pair_out=torch.empty((T * k, H), dtype=torch.float16, device=d),
+                pair_scale=torch.empty((T * k,), dtype=torch.float32, device=d),
                 pair_sqnorm=torch.empty((T * k,), dtype=torch.float32, device=d) if reap else None,
                 h_codes=torch.empty((T * k, I // 2), dtype=torch.uint8, device=d),
                 h_scales=torch.empty((T * k, I // 16), dtype=torch.uint8, device=d),
@@ -157,23 +159,24 @@ class NVFP4MoELayer:
                                      workspace=b["ffn_ws"])
         mark(2)
         ops.moe_nvfp4_down_scatter(b["h_codes"], b["h_scales"], self.h_gs, T, *self.w2, self.k, r.expert_offsets,
-                                   r.sorted_pair_ids, r.topk_w, pair_out=b["pair_out"],
+                                   r.sorted_pair_ids, r.topk_w, pair_out=b["pair_out"], pair_scale=b["pair_scale"],
                                    pair_sqnorm=b["pair_sqnorm"] if reap else None, workspace=b["ffn_ws"])
         mark(3)
         sal = None
         if block:
             torch.cuda.current_stream(self.device).wait_event(b["ev_shared"])
-            ops.moe_combine_block(b["pair_out"], b["shared_out"], T, self.k, out_dtype, y=b["y"])
+            ops.moe_combine_block(b["pair_out"], b["pair_scale"], b["shared_out"], T, self.k, out_dtype, y=b["y"])
             if reap:
                 sal = ops.reap_saliency(b["pair_sqnorm"], r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, self.k,
                                         self.E, out=b["saliency"])
         elif reap:  # the combine and the saliency in one launch
-            _, sal = ops.moe_combine_reap(b["pair_out"], T, self.k, b["pair_sqnorm"], r.topk_w, r.expert_offsets,
-                                          r.sorted_pair_ids, self.E, out_dtype, y=b["y"], saliency=b["saliency"])
+            _, sal = ops.moe_combine_reap(b["pair_out"], b["pair_scale"], T, self.k, b["pair_sqnorm"], r.topk_w,
+                                          r.expert_offsets, r.sorted_pair_ids, self.E, out_dtype, y=b["y"],
+                                          saliency=b["saliency"])
         else:
-            ops.moe_combine(b["pair_out"], T, self.k, out_dtype, y=b["y"])
+            ops.moe_combine(b["pair_out"], b["pair_scale"], T, self.k, out_dtype, y=b["y"])
         mark(4)
-        return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_sqnorm"], sal,
+        return LayerOut(b["y"], r, b["x_codes"], b["x_scales"], b["pair_out"], b["pair_scale"], b["pair_sqnorm"], sal,
                         b.get("shared_out"), b["h_codes"], b["h_scales"])
 
     __call__ = forward

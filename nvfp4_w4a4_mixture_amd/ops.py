@@ -181,9 +181,27 @@ def _ffn_dims(x_codes, w13_codes, w2_codes):
     return T, 2 * h_half, E, two_i // 2
 
 
+def _pair_outputs(npairs: int, H: int, dev, pair_out, pair_scale, pair_sqnorm):
+    """The pair-row outputs: given ones checked, missing ones allocated (pair_sqnorm True: allocate, None/False: skip)."""
+    if pair_out is None:
+        pair_out = torch.empty((npairs, H), dtype=torch.float16, device=dev)
+    if pair_scale is None:
+        pair_scale = torch.empty((npairs,), dtype=torch.float32, device=dev)
+    _need(pair_out, "pair_out", torch.float16, (npairs, H))
+    _need(pair_scale, "pair_scale", torch.float32, (npairs,))
+    if pair_sqnorm is True:
+        pair_sqnorm = torch.empty((npairs,), dtype=torch.float32, device=dev)
+    elif pair_sqnorm is False:
+        pair_sqnorm = None
+    if pair_sqnorm is not None:
+        _need(pair_sqnorm, "pair_sqnorm", torch.float32, (npairs,))
+    return pair_out, pair_scale, pair_sqnorm
+
+
 def moe_nvfp4_grouped_ffn(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales, w2_gs,
-                          h_gs, k: int, expert_offsets, sorted_pair_ids, topk_w, pair_out=None,
+                          h_gs, k: int, expert_offsets, sorted_pair_ids, topk_w, pair_out=None, pair_scale=None,
                           pair_sqnorm: Optional[torch.Tensor] | bool = None, workspace=None, stream=None):
+    """Returns (pair_out, pair_scale, pair_sqnorm): pair row p is pair_out[p] (FP16) * pair_scale[p]."""
     T, H, E, I = _ffn_dims(x_codes, w13_codes, w2_codes)
     _need(x_codes, "x_codes", torch.uint8, (T, H // 2))
     _need(x_scales, "x_scales", torch.uint8, (T, H // 16))
@@ -199,23 +217,18 @@ def moe_nvfp4_grouped_ffn(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs
     _need(sorted_pair_ids, "sorted_pair_ids", torch.int32, (T * k,))
     _need(topk_w, "topk_w", torch.float32)
     dev = x_codes.device
-    if pair_out is None:
-        pair_out = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    if pair_sqnorm is True:
-        pair_sqnorm = torch.empty((T * k,), dtype=torch.float32, device=dev)
-    elif pair_sqnorm is False:
-        pair_sqnorm = None
+    pair_out, pair_scale, pair_sqnorm = _pair_outputs(T * k, H, dev, pair_out, pair_scale, pair_sqnorm)
     ws = _workspace(moe_ffn_workspace_bytes(T, k, E, H, I), dev, workspace)
     st = lib().moe_nvfp4_grouped_ffn(_p(x_codes), _p(x_scales), _p(x_gs), T, H, _p(w13_codes), _p(w13_scales),
                                      _p(w13_gs), _p(w2_codes), _p(w2_scales), _p(w2_gs), _p(h_gs), E, I, k,
                                      _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w), _p(pair_out),
-                                     _p(pair_sqnorm), _p(ws), ws.numel(), _stream(stream))
+                                     _p(pair_scale), _p(pair_sqnorm), _p(ws), ws.numel(), _stream(stream))
     check(st, "moe_nvfp4_grouped_ffn")
-    return pair_out, pair_sqnorm
+    return pair_out, pair_scale, pair_sqnorm
 
 
 def moe_nvfp4_grouped_ffn_noalloc(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs, w2_codes, w2_scales,
-                                  w2_gs, h_gs, k: int, expert_offsets, sorted_pair_ids, topk_w, pair_out,
+                                  w2_gs, h_gs, k: int, expert_offsets, sorted_pair_ids, topk_w, pair_out, pair_scale,
                                   pair_sqnorm: Optional[torch.Tensor] = None, stream=None):
     """moe_nvfp4_grouped_ffn on the library's static scratch: the caller passes every output
     (nothing is allocated here or in the library, so the call can be captured in a graph)."""
@@ -233,15 +246,16 @@ def moe_nvfp4_grouped_ffn_noalloc(x_codes, x_scales, x_gs, w13_codes, w13_scales
     _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
     _need(sorted_pair_ids, "sorted_pair_ids", torch.int32, (T * k,))
     _need(topk_w, "topk_w", torch.float32)
-    _need(pair_out, "pair_out", torch.float32, (T * k, H))
+    _need(pair_out, "pair_out", torch.float16, (T * k, H))
+    _need(pair_scale, "pair_scale", torch.float32, (T * k,))
     if pair_sqnorm is not None:
         _need(pair_sqnorm, "pair_sqnorm", torch.float32, (T * k,))
     st = lib().moe_nvfp4_grouped_ffn_noalloc(_p(x_codes), _p(x_scales), _p(x_gs), T, H, _p(w13_codes),
                                              _p(w13_scales), _p(w13_gs), _p(w2_codes), _p(w2_scales), _p(w2_gs),
                                              _p(h_gs), E, I, k, _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w),
-                                             _p(pair_out), _p(pair_sqnorm), _stream(stream))
+                                             _p(pair_out), _p(pair_scale), _p(pair_sqnorm), _stream(stream))
     check(st, "moe_nvfp4_grouped_ffn_noalloc")
-    return pair_out, pair_sqnorm
+    return pair_out, pair_scale, pair_sqnorm
 
 
 def moe_nvfp4_gate_up_swiglu(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13_gs, h_gs, k: int,
@@ -266,49 +280,56 @@ def moe_nvfp4_gate_up_swiglu(x_codes, x_scales, x_gs, w13_codes, w13_scales, w13
 
 
 def moe_nvfp4_down_scatter(h_codes, h_scales, h_gs, T: int, w2_codes, w2_scales, w2_gs, k: int, expert_offsets,
-                           sorted_pair_ids, topk_w, pair_out=None, pair_sqnorm=None, workspace=None, stream=None):
+                           sorted_pair_ids, topk_w, pair_out=None, pair_scale=None, pair_sqnorm=None, workspace=None,
+                           stream=None):
+    """Returns (pair_out, pair_scale, pair_sqnorm), as moe_nvfp4_grouped_ffn."""
     E, H, i_half = w2_codes.shape
     I = 2 * i_half
     _need(h_codes, "h_codes", torch.uint8, (T * k, I // 2))
     dev = h_codes.device
-    if pair_out is None:
-        pair_out = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    if pair_sqnorm is True:
-        pair_sqnorm = torch.empty((T * k,), dtype=torch.float32, device=dev)
-    elif pair_sqnorm is False:
-        pair_sqnorm = None
+    pair_out, pair_scale, pair_sqnorm = _pair_outputs(T * k, H, dev, pair_out, pair_scale, pair_sqnorm)
     ws = _workspace(moe_ffn_stage_workspace_bytes(T, k, E, H, I), dev, workspace)
     st = lib().moe_nvfp4_down_scatter(_p(h_codes), _p(h_scales), _p(h_gs), T, H, _p(w2_codes), _p(w2_scales),
                                       _p(w2_gs), E, I, k, _p(expert_offsets), _p(sorted_pair_ids), _p(topk_w),
-                                      _p(pair_out), _p(pair_sqnorm), _p(ws), ws.numel(), _stream(stream))
+                                      _p(pair_out), _p(pair_scale), _p(pair_sqnorm), _p(ws), ws.numel(),
+                                      _stream(stream))
     check(st, "moe_nvfp4_down_scatter")
-    return pair_out, pair_sqnorm
+    return pair_out, pair_scale, pair_sqnorm
 
 
-def moe_combine(pair_out: torch.Tensor, T: int, k: int, out_dtype: torch.dtype = torch.bfloat16, y=None,
-                stream=None) -> torch.Tensor:
-    _need(pair_out, "pair_out", torch.float32)
-    H = pair_out.shape[1]
+def _need_pairs(pair_out: torch.Tensor, pair_scale: torch.Tensor, T: int, k: int) -> int:
+    _need(pair_out, "pair_out", torch.float16)
+    if pair_out.dim() != 2 or pair_out.shape[0] < T * k:
+        raise ValueError(f"pair_out must be [>= T*k, H], got {tuple(pair_out.shape)}")
+    _need(pair_scale, "pair_scale", torch.float32)
+    if pair_scale.numel() < T * k:
+        raise ValueError(f"pair_scale must hold T*k = {T * k} scales, got {pair_scale.numel()}")
+    return pair_out.shape[1]
+
+
+def moe_combine(pair_out: torch.Tensor, pair_scale: torch.Tensor, T: int, k: int,
+                out_dtype: torch.dtype = torch.bfloat16, y=None, stream=None) -> torch.Tensor:
+    H = _need_pairs(pair_out, pair_scale, T, k)
     code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
     if y is None:
         y = torch.empty((T, H), dtype=out_dtype, device=pair_out.device)
-    st = lib().moe_combine(_p(pair_out), T, k, H, code, _p(y), _stream(stream))
+    st = lib().moe_combine(_p(pair_out), _p(pair_scale), T, k, H, code, _p(y), _stream(stream))
     check(st, "moe_combine")
     return y
 
 
-def moe_combine_reap(pair_out: torch.Tensor, T: int, k: int, pair_sqnorm, topk_w, expert_offsets, sorted_pair_ids,
-                     E: int, out_dtype: torch.dtype = torch.bfloat16, y=None, saliency=None, stream=None):
+def moe_combine_reap(pair_out: torch.Tensor, pair_scale: torch.Tensor, T: int, k: int, pair_sqnorm, topk_w,
+                     expert_offsets, sorted_pair_ids, E: int, out_dtype: torch.dtype = torch.bfloat16, y=None,
+                     saliency=None, stream=None):
     """moe_combine and reap_saliency in one launch: (y, saliency)."""
-    _need(pair_out, "pair_out", torch.float32)
-    H = pair_out.shape[1]
+    H = _need_pairs(pair_out, pair_scale, T, k)
     code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
     if y is None:
         y = torch.empty((T, H), dtype=out_dtype, device=pair_out.device)
     if saliency is None:
         saliency = torch.empty((E,), dtype=torch.float32, device=pair_out.device)
-    st = lib().moe_combine_reap(_p(pair_out), T, k, H, code, _p(y), _p(pair_sqnorm), _p(topk_w), _p(expert_offsets),
-                                _p(sorted_pair_ids), E, _p(saliency), _stream(stream))
+    st = lib().moe_combine_reap(_p(pair_out), _p(pair_scale), T, k, H, code, _p(y), _p(pair_sqnorm), _p(topk_w),
+                                _p(expert_offsets), _p(sorted_pair_ids), E, _p(saliency), _stream(stream))
     check(st, "moe_combine_reap")
     return y, saliency
 
@@ -413,16 +434,15 @@ def moe_shared_down(h_bf16, w2_bf16, out=None, workspace=None, stream=None) -> t
     return out
 
 
-def moe_combine_block(pair_out: torch.Tensor, shared_out: torch.Tensor, T: int, k: int,
+def moe_combine_block(pair_out: torch.Tensor, pair_scale: torch.Tensor, shared_out: torch.Tensor, T: int, k: int,
                       out_dtype: torch.dtype = torch.bfloat16, y=None, stream=None) -> torch.Tensor:
     """y = routed combine + shared expert output."""
-    _need(pair_out, "pair_out", torch.float32)
-    H = pair_out.shape[1]
+    H = _need_pairs(pair_out, pair_scale, T, k)
     _need(shared_out, "shared_out", torch.float32, (T, H))
     code = {torch.bfloat16: 0, torch.float32: 1}[out_dtype]
     if y is None:
         y = torch.empty((T, H), dtype=out_dtype, device=pair_out.device)
-    st = lib().moe_combine_block(_p(pair_out), _p(shared_out), T, k, H, code, _p(y), _stream(stream))
+    st = lib().moe_combine_block(_p(pair_out), _p(pair_scale), _p(shared_out), T, k, H, code, _p(y), _stream(stream))
     check(st, "moe_combine_block")
     return y
 

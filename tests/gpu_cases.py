@@ -36,6 +36,26 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def pair_rows(pair_out: torch.Tensor, pair_scale: torch.Tensor) -> np.ndarray:
+    """FP64 pair rows from the FP16 values and their power-of-two row scales (exact)."""
+    return to_np(pair_out).astype(np.float64) * to_np(pair_scale).astype(np.float64)[:, None]
+
+
+def expected_pair_scale(topk_w: np.ndarray, ids: np.ndarray, I: int, h_gs: np.ndarray, w2_gs: np.ndarray) -> np.ndarray:
+    """The row scales the library's pair-row format states: 2^E, E = floor(log2(B)) - 14 clamped to [-126, 113],
+    B = |w_p| * (I * 2688^2) * (1 / (h_gs[e] * w2_gs[e])) in FP32 operations in that order."""
+    f32 = np.float32
+    w = np.abs(np.asarray(topk_w, f32).reshape(-1))
+    e = np.asarray(ids).reshape(-1)
+    alpha = f32(1.0) / (np.asarray(h_gs, f32)[e] * np.asarray(w2_gs, f32)[e])
+    with np.errstate(over="ignore", invalid="ignore"):
+        bound = (w * f32(f32(I) * f32(7225344.0))) * alpha
+    bits = bound.view(np.uint32)
+    eb = ((bits >> 23) & 255).astype(np.int64) - 127
+    E = np.clip(eb - 14, -126, 113)
+    return np.ldexp(np.float32(1.0), E).astype(np.float32)
+
+
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

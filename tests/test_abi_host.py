@@ -108,13 +108,14 @@ def test_quantize_weights_validation(L):
     assert q(P, 0, 16, 128, P, P, P, None) == OK
 
 
-def _ffn(L, T=16, H=256, E=8, I=128, k=2, ws=P2, wsb=1 << 30, xc=P, sq=None, po=P):
-    return L.moe_nvfp4_grouped_ffn(xc, P, P, T, H, P, P, P, P, P, P, P, E, I, k, P, P, P, po, sq, ws, wsb, None)
+def _ffn(L, T=16, H=256, E=8, I=128, k=2, ws=P2, wsb=1 << 30, xc=P, sq=None, po=P, ps=P):
+    return L.moe_nvfp4_grouped_ffn(xc, P, P, T, H, P, P, P, P, P, P, P, E, I, k, P, P, P, po, ps, sq, ws, wsb, None)
 
 
 def test_ffn_validation(L):
     assert _ffn(L, xc=None) == NULL
     assert _ffn(L, po=None) == NULL
+    assert _ffn(L, ps=None) == NULL
     assert _ffn(L, H=200) == SHAPE  # H % 256
     assert _ffn(L, I=96) == SHAPE  # I % 128
     assert _ffn(L, k=9, E=8) == SHAPE
@@ -124,8 +125,10 @@ def test_ffn_validation(L):
     assert _ffn(L, wsb=16) == WORKSPACE
     assert _ffn(L, xc=ctypes.c_void_p(0x10008)) == ALIGN
     assert _ffn(L, po=ctypes.c_void_p(0x10004)) == ALIGN
+    assert _ffn(L, ps=ctypes.c_void_p(0x10002)) == ALIGN
+    assert _ffn(L, ps=ctypes.c_void_p(0x10004)) == _ffn(L)  # 4-byte alignment is enough for pair_scale
     assert L.moe_nvfp4_grouped_ffn(P, ctypes.c_void_p(0x10004), P, 16, 256, P, P, P, P, P, P, P, 8, 128, 2, P, P, P,
-                                   P, None, P2, 1 << 30, None) == ALIGN  # x_scales 16-byte aligned
+                                   P, P, None, P2, 1 << 30, None) == ALIGN  # x_scales 16-byte aligned
     assert _ffn(L, ws=ctypes.c_void_p(0x10010)) == ALIGN
     assert _ffn(L, T=0) == OK  # no pairs: no-op
 
@@ -150,7 +153,7 @@ def test_ffn_rejects_shapes_past_32bit_offsets(L):
     g = L.moe_nvfp4_gate_up_swiglu
     assert g(P, P, P, t_max + 1, 6144, P, P, P, P, 8, 128, 1, P, P, P, P, P2, big, None) == SHAPE
     d = L.moe_nvfp4_down_scatter
-    assert d(P, P, P, 524288, 256, P, P, P, 80, 2048, 8, P, P, P, P, None, P2, big, None) == SHAPE
+    assert d(P, P, P, 524288, 256, P, P, P, 80, 2048, 8, P, P, P, P, P, None, P2, big, None) == SHAPE
 
 
 def test_noalloc_ffn_validation(L):
@@ -159,7 +162,7 @@ def test_noalloc_ffn_validation(L):
     f = L.moe_nvfp4_grouped_ffn_noalloc
 
     def call(T=16, H=256, E=8, I=128, k=2, xc=P, po=P):
-        return f(xc, P, P, T, H, P, P, P, P, P, P, P, E, I, k, P, P, P, po, None, None)
+        return f(xc, P, P, T, H, P, P, P, P, P, P, P, E, I, k, P, P, P, po, P, None, None)
 
     assert call(xc=None) == NULL
     assert call(H=200) == SHAPE
@@ -186,18 +189,23 @@ def test_stage_validation(L):
     assert g(P, P, P, 16, 256, P, P, P, P, 8, 128, 2, P, P, None, P, P2, 1 << 30, None) == NULL
     assert g(P, P, P, 16, 100, P, P, P, P, 8, 128, 2, P, P, P, P, P2, 1 << 30, None) == SHAPE
     d = L.moe_nvfp4_down_scatter
-    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, None, P, None, P2, 1 << 30, None) == NULL
-    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, P, P, None, None, 0, None) == WORKSPACE
+    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, None, P, P, None, P2, 1 << 30, None) == NULL
+    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, P, P, None, None, P2, 1 << 30, None) == NULL  # pair_scale
+    assert d(P, P, P, 16, 256, P, P, P, 8, 128, 2, P, P, P, P, P, None, None, 0, None) == WORKSPACE
 
 
 def test_combine_and_reap_validation(L):
     c = L.moe_combine
-    assert c(None, 4, 2, 64, 0, P, None) == NULL
-    assert c(P, 4, 2, 66, 0, P, None) == SHAPE
-    assert c(P, 4, 2, 64, 2, P, None) == SHAPE
-    assert c(P, 4, 0, 64, 0, P, None) == SHAPE
-    assert c(P, 4, 2, 64, 0, ctypes.c_void_p(0x10004), None) == ALIGN
-    assert c(P, 0, 2, 64, 0, P, None) == OK
+    assert c(None, P, 4, 2, 64, 0, P, None) == NULL
+    assert c(P, None, 4, 2, 64, 0, P, None) == NULL
+    assert c(P, P, 4, 2, 66, 0, P, None) == SHAPE
+    assert c(P, P, 4, 2, 68, 0, P, None) == SHAPE  # H % 8: eight FP16 columns per 16-byte load
+    assert c(P, P, 4, 2, 64, 2, P, None) == SHAPE
+    assert c(P, P, 4, 0, 64, 0, P, None) == SHAPE
+    assert c(P, P, 4, 2, 64, 0, ctypes.c_void_p(0x10004), None) == ALIGN
+    assert c(ctypes.c_void_p(0x10008), P, 4, 2, 64, 0, P, None) == ALIGN
+    assert c(P, ctypes.c_void_p(0x10002), 4, 2, 64, 0, P, None) == ALIGN
+    assert c(P, 0, 0, 2, 64, 0, P, None) == OK
     r = L.reap_saliency
     assert r(P, P, P, None, 4, 2, 8, P, None) == NULL
     assert r(P, P, P, P, 4, 2, 0, P, None) == SHAPE
@@ -242,8 +250,10 @@ def test_shared_and_rotation_validation(L):
     e = L.moe_shared_expert
     assert e(P, 4, 256, 256, P, P, 128, P, P, 16, None) == WORKSPACE
     c = L.moe_combine_block
-    assert c(P, None, 4, 2, 64, 0, P, None) == NULL
-    assert c(P, P, 4, 2, 66, 0, P, None) == SHAPE
+    assert c(P, P, None, 4, 2, 64, 0, P, None) == NULL
+    assert c(P, None, P, 4, 2, 64, 0, P, None) == NULL
+    assert c(P, P, P, 4, 2, 66, 0, P, None) == SHAPE
+    assert c(P, ctypes.c_void_p(0x10002), P, 4, 2, 64, 0, P, None) == ALIGN
     r = L.hadamard_rotate_bf16
     assert r(P, 4, 256, 256, None, 48, P2, 256, None) == SHAPE  # block not a power of two
     assert r(P, 4, 256, 256, None, 512, P2, 256, None) == SHAPE  # block > cols
@@ -257,10 +267,12 @@ def test_shared_and_rotation_validation(L):
 
 def test_combine_reap_validation(L):
     f = L.moe_combine_reap
-    assert f(P, 4, 2, 66, 0, P, P, P, P, P, 8, P, None) == SHAPE
-    assert f(P, 4, 2, 64, 0, P, P, P, P, P, 0, P, None) == SHAPE
-    assert f(P, 4, 2, 64, 0, P, None, P, P, P, 8, P, None) == NULL
-    assert f(P, 4, 2, 64, 0, ctypes.c_void_p(0x10004), P, P, P, P, 8, P, None) == ALIGN
+    assert f(P, P, 4, 2, 66, 0, P, P, P, P, P, 8, P, None) == SHAPE
+    assert f(P, P, 4, 2, 64, 0, P, P, P, P, P, 0, P, None) == SHAPE
+    assert f(P, P, 4, 2, 64, 0, P, None, P, P, P, 8, P, None) == NULL
+    assert f(P, None, 4, 2, 64, 0, P, P, P, P, P, 8, P, None) == NULL
+    assert f(P, P, 4, 2, 64, 0, ctypes.c_void_p(0x10004), P, P, P, P, 8, P, None) == ALIGN
+    assert f(P, ctypes.c_void_p(0x10002), 4, 2, 64, 0, P, P, P, P, P, 8, P, None) == ALIGN
 
 
 def test_prepack_validation(L):

@@ -37,7 +37,7 @@ def test_stage_bytes_and_flops_decode_shape(bench):
     x_bytes = cfg.T * (cfg.H // 2 + cfg.H // 16)
     h_bytes = pairs * (cfg.I // 2 + cfg.I // 16)
     assert r["gate_up"]["bytes"] == 54 * w13 + x_bytes + h_bytes == 764_614_656
-    assert r["down"]["bytes"] == 54 * w2 + h_bytes + pairs * cfg.H * 4
+    assert r["down"]["bytes"] == 54 * w2 + h_bytes + pairs * (cfg.H * 2 + 4)  # FP16 pair rows + row scales
     # FLOPs per pair: 2 H 2I (gate_up) + 2 I H (down)
     assert r["gate_up"]["flops"] + r["down"]["flops"] == pairs * 75_497_472
 

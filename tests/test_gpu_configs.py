@@ -34,7 +34,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_cases import bf16_round, check_routing, rel_l2, say, to_np, untile_weight_scales
+from gpu_cases import bf16_round, check_routing, pair_rows, rel_l2, say, to_np, untile_weight_scales
 from oracle import moe as omoe
 from oracle import nvfp4 as onv
 from oracle import reap as oreap
@@ -188,7 +188,7 @@ def test_full_size_workload(ci):
     f = omoe.expert_pairs_output(xb[toks], gs_x, experts[whole], gs_h[whole])
     wp = w64_ref.reshape(-1)[pairs]
     pairs_d = torch.from_numpy(pairs.astype(np.int64)).cuda()
-    po = to_np(out.pair_out[pairs_d])
+    po = pair_rows(out.pair_out[pairs_d], out.pair_scale[pairs_d])
     perr = rel_l2(po, wp[:, None] * f)
     norms = np.linalg.norm(f, axis=1)
     sq = to_np(out.pair_sqnorm[pairs_d]).astype(np.float64)
@@ -202,7 +202,7 @@ def test_full_size_workload(ci):
     hs = to_np(out.h_scales[offsets[whole]:offsets[whole + 1]])
     code_diff = float(np.mean(hc != onv.pack_codes(hc_ref)))
     scale_diff = float(np.mean(hs != hs_ref))
-    print(f"  pair_out rel-L2 {perr:.3e}, max ||f|| rel err {nerr:.3e}; h code bytes differing {code_diff:.2e}, "
+    print(f"  pair rows rel-L2 {perr:.3e}, max ||f|| rel err {nerr:.3e}; h code bytes differing {code_diff:.2e}, "
           f"h scales differing {scale_diff:.2e}", flush=True)
     assert perr <= 2e-3
     assert nerr <= 1e-3

@@ -16,8 +16,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_cases import (bf16_round, check_routing, config_case, dev_bf16, gpu_layer, oracle_codes, oracle_layer,
-                       oracle_perm, random_case, rel_l2, say, to_np, untile_weight_scales)
+from gpu_cases import (bf16_round, check_routing, config_case, dev_bf16, expected_pair_scale, gpu_layer, oracle_codes,
+                       oracle_layer, oracle_perm, pair_rows, random_case, rel_l2, say, to_np, untile_weight_scales)
 from oracle import nvfp4 as onv
 from oracle import routing as oroute
 from workloads import by_name, gen
@@ -279,9 +279,13 @@ def _layer_check(ops, case, reap=True):
     y32 = to_np(out32.y)
     err = rel_l2(y32, ref["y"])
     pair_ref = ref["pair_f"] * ref["weights64"].reshape(-1)[:, None]
-    perr = rel_l2(to_np(out32.pair_out), pair_ref)
-    print(f"  rel-L2 y(fp32)={err:.3e} pair_out={perr:.3e}", flush=True)
+    perr = rel_l2(pair_rows(out32.pair_out, out32.pair_scale), pair_ref)
+    print(f"  rel-L2 y(fp32)={err:.3e} pair rows={perr:.3e}", flush=True)
     assert err <= Y_TOL and perr <= Y_TOL
+    # the row scales follow the stated rule exactly; the FP16 values stay below 2^15
+    ps = to_np(out32.pair_scale)
+    assert np.array_equal(ps, expected_pair_scale(w, ids, case.I, to_np(layer.h_gs), to_np(layer.w2[2])))
+    assert float(out32.pair_out.abs().max()) < 2.0 ** 15
     if reap:
         sal = to_np(out32.saliency).astype(np.float64)
         cnt = np.bincount(ids.reshape(-1), minlength=case.E)
@@ -354,6 +358,55 @@ def test_layer_parity_subnormal_weight_scales(ops, T):
     _layer_check(ops, case)
 
 
+@pytest.mark.parametrize("name,T,xscale,wscale", [
+    ("large_outputs", 40, 1.0, 2.0),  # pair rows up to about 9e4: past FP16's largest finite value
+    ("large_outputs_decode", 9, 1.0, 2.0),
+    ("tiny_outputs", 40, 1e-4, 0.02),  # pair rows about 1e-9: below FP16's smallest subnormal
+    ("tiny_outputs_decode", 9, 1e-4, 0.02),
+])
+def test_layer_parity_output_range(ops, name, T, xscale, wscale):
+    """Pair rows are FP16 times a power-of-two row scale: outputs far outside FP16's own range keep full precision."""
+    case = random_case(name, 5, T, 256, 128, 8, 2, xscale=xscale, wscale=wscale)
+    ref = oracle_layer(case, with_pairs=True)
+    peak = float(np.abs(ref["pair_f"] * ref["weights64"].reshape(-1)[:, None]).max())
+    assert peak > 65504.0 if wscale > 1 else peak < 2.0 ** -24
+    _layer_check(ops, case)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_combine_decodes_scaled_fp16_rows(ops, out_dtype):
+    """y = sum over j, in j order, of FP16 value times its row scale, in FP32: bit for bit against numpy, for FP16
+    values across their whole finite range and scales from 2^-100 to 2^100; the block combine adds the shared
+    row last."""
+    rng = np.random.default_rng(3)
+    T, k, H = 37, 5, 264
+    bits = rng.integers(0, 1 << 16, (T * k, H), dtype=np.uint16)
+    bits[(bits & 0x7C00) == 0x7C00] &= 0xBFFF  # no inf or NaN: clear the top exponent bit
+    vals = bits.view(np.float16)
+    scale = np.ldexp(np.float32(1.0), rng.integers(-100, 101, T * k)).astype(np.float32)
+    # a third of the tokens: every row at one scale, so that sums cancel and round
+    same = rng.random(T) < 0.33
+    scale.reshape(T, k)[same] = np.float32(2.0 ** 7)
+    shared = (rng.standard_normal((T, H)) * 1e3).astype(np.float32)
+    d = vals.astype(np.float32) * scale[:, None]  # exact
+    y = d.reshape(T, k, H)[:, 0].copy()
+    for j in range(1, k):
+        y = (y + d.reshape(T, k, H)[:, j]).astype(np.float32)
+    yb = (y + shared).astype(np.float32)
+    po = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.float16)
+    ps = torch.from_numpy(scale).cuda()
+    say(f"combine of scaled FP16 rows, {out_dtype}")
+    got = ops.moe_combine(po, ps, T, k, out_dtype)
+    got_b = ops.moe_combine_block(po, ps, torch.from_numpy(shared).cuda(), T, k, out_dtype)
+    torch.cuda.synchronize()
+    if out_dtype == torch.float32:
+        assert np.array_equal(to_np(got).view(np.uint32), y.view(np.uint32))
+        assert np.array_equal(to_np(got_b).view(np.uint32), yb.view(np.uint32))
+    else:
+        assert np.array_equal(to_np(got.view(torch.int16)).view(np.uint16), gen.f32_to_bf16_bits(y))
+        assert np.array_equal(to_np(got_b.view(torch.int16)).view(np.uint16), gen.f32_to_bf16_bits(yb))
+
+
 def test_single_expert_output_is_rsf_times_mlp(ops):
     case = random_case("e1", 11, 24, 256, 128, 1, 1)
     layer, out, ref = _layer_check(ops, case, reap=False)
@@ -368,11 +421,11 @@ def test_grouped_ffn_matches_stage_calls(ops, T):
     x = dev_bf16(case.x)
     out = layer(x, out_dtype=torch.float32, reap=True)  # the layer calls the two stage entry points
     r = out.route
-    pair_out, sq = ops.moe_nvfp4_grouped_ffn(out.x_codes, out.x_scales, layer.x_gs, *layer.w13, *layer.w2,
-                                             layer.h_gs, case.k, r.expert_offsets, r.sorted_pair_ids, r.topk_w,
-                                             pair_sqnorm=True)
+    pair_out, pair_scale, sq = ops.moe_nvfp4_grouped_ffn(out.x_codes, out.x_scales, layer.x_gs, *layer.w13,
+                                                         *layer.w2, layer.h_gs, case.k, r.expert_offsets,
+                                                         r.sorted_pair_ids, r.topk_w, pair_sqnorm=True)
     torch.cuda.synchronize()
-    assert torch.equal(pair_out, out.pair_out)
+    assert torch.equal(pair_out, out.pair_out) and torch.equal(pair_scale, out.pair_scale)
     assert torch.equal(sq, out.pair_sqnorm)
 
 
@@ -403,7 +456,7 @@ def test_repeat_runs_are_bitwise_identical(ops, name, T, H, I, E, k):
 
     def snap(o):
         return [o.y, o.saliency, o.route.topk_ids, o.route.topk_w, o.route.expert_offsets, o.route.sorted_pair_ids,
-                o.x_codes, o.x_scales, o.h_codes, o.h_scales, o.pair_out, o.pair_sqnorm]
+                o.x_codes, o.x_scales, o.h_codes, o.h_scales, o.pair_out, o.pair_scale, o.pair_sqnorm]
 
     first = [t.clone() for t in snap(layer(x, out_dtype=torch.float32, reap=True))]
     for _ in range(2):
@@ -458,14 +511,15 @@ def test_combine_reap_equals_separate_calls(ops, T):
     say(f"combine + reap fused vs separate, T={T}")
     out = layer(dev_bf16(case.x), out_dtype=torch.bfloat16, reap=True)  # the layer's fused launch
     r = out.route
-    y2 = ops.moe_combine(out.pair_out, T, case.k, torch.bfloat16)
+    y2 = ops.moe_combine(out.pair_out, out.pair_scale, T, case.k, torch.bfloat16)
     s2 = ops.reap_saliency(out.pair_sqnorm, r.topk_w, r.expert_offsets, r.sorted_pair_ids, T, case.k, case.E)
     torch.cuda.synchronize()
     assert torch.equal(out.y, y2) and torch.equal(out.saliency, s2)
     # no tokens: zero saliencies, nothing else written
     e = torch.full((case.E,), 7.0, device="cuda")
     off = torch.zeros((case.E + 1,), dtype=torch.int32, device="cuda")
-    empty = torch.empty((0, 512), dtype=torch.float32, device="cuda")
-    ops.moe_combine_reap(empty, 0, case.k, None, None, off, None, case.E, saliency=e)
+    empty = torch.empty((0, 512), dtype=torch.float16, device="cuda")
+    no_scales = torch.empty((0,), dtype=torch.float32, device="cuda")
+    ops.moe_combine_reap(empty, no_scales, 0, case.k, None, None, off, None, case.E, saliency=e)
     torch.cuda.synchronize()
     assert torch.all(e == 0)

@@ -1,6 +1,6 @@
 """moe_nvfp4_grouped_ffn_noalloc (the grouped FFN on the library's static scratch,
 for callers that cannot allocate) against moe_nvfp4_grouped_ffn with a caller
-workspace: pair outputs and sums of squares bitwise equal, on calls in a row
+workspace: pair rows (FP16 values and row scales) and sums of squares bitwise equal, on calls in a row
 whose inputs shrink (the tiled kernels, then the decode kernels), so the second
 and third calls run on scratch the earlier ones left behind."""
 
@@ -27,24 +27,29 @@ def test_noalloc_matches_workspace_call_on_shrinking_inputs(ops):
         layer = gpu_layer(case)
         r, xc, xs = ops.moe_route_quantize(dev_bf16(case.x), layer.w_router, layer.bias, case.k, case.rsf, layer.x_gs)
         n, H = T * case.k, case.H
-        po_ref = torch.empty((n, H), dtype=torch.float32, device="cuda")
+        po_ref = torch.empty((n, H), dtype=torch.float16, device="cuda")
+        ps_ref = torch.empty((n,), dtype=torch.float32, device="cuda")
         sq_ref = torch.empty((n,), dtype=torch.float32, device="cuda")
         ops.moe_nvfp4_grouped_ffn(xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k, r.expert_offsets,
-                                  r.sorted_pair_ids, r.topk_w, pair_out=po_ref, pair_sqnorm=sq_ref)
-        po = torch.full((n, H), float("nan"), dtype=torch.float32, device="cuda")
+                                  r.sorted_pair_ids, r.topk_w, pair_out=po_ref, pair_scale=ps_ref, pair_sqnorm=sq_ref)
+        po = torch.full((n, H), float("nan"), dtype=torch.float16, device="cuda")
+        ps = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
         sq = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
         ops.moe_nvfp4_grouped_ffn_noalloc(xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k,
-                                          r.expert_offsets, r.sorted_pair_ids, r.topk_w, po, sq)
+                                          r.expert_offsets, r.sorted_pair_ids, r.topk_w, po, ps, sq)
         torch.cuda.synchronize()
         assert torch.equal(po, po_ref), f"{name}: pair_out differs"
+        assert torch.equal(ps, ps_ref), f"{name}: pair_scale differs"
         assert torch.equal(sq, sq_ref), f"{name}: pair_sqnorm differs"
-        assert bool(torch.isfinite(po).all())
+        assert bool(torch.isfinite(po).all()) and bool(torch.isfinite(ps).all())
         # and without the sums of squares
-        po2 = torch.full((n, H), float("nan"), dtype=torch.float32, device="cuda")
+        po2 = torch.full((n, H), float("nan"), dtype=torch.float16, device="cuda")
+        ps2 = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
         ops.moe_nvfp4_grouped_ffn_noalloc(xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k,
-                                          r.expert_offsets, r.sorted_pair_ids, r.topk_w, po2, None)
+                                          r.expert_offsets, r.sorted_pair_ids, r.topk_w, po2, ps2, None)
         torch.cuda.synchronize()
         assert torch.equal(po2, po_ref), f"{name}: pair_out differs without pair_sqnorm"
+        assert torch.equal(ps2, ps_ref), f"{name}: pair_scale differs without pair_sqnorm"
 
 
 def test_noalloc_captured_in_a_graph(ops):
@@ -57,14 +62,16 @@ def test_noalloc_captured_in_a_graph(ops):
     layer = gpu_layer(case)
     r, xc, xs = ops.moe_route_quantize(dev_bf16(case.x), layer.w_router, layer.bias, case.k, case.rsf, layer.x_gs)
     n, H = case.T * case.k, case.H
-    po_ref = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    po_ref = torch.empty((n, H), dtype=torch.float16, device="cuda")
+    ps_ref = torch.empty((n,), dtype=torch.float32, device="cuda")
     sq_ref = torch.empty((n,), dtype=torch.float32, device="cuda")
     ops.moe_nvfp4_grouped_ffn(xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k, r.expert_offsets,
-                              r.sorted_pair_ids, r.topk_w, pair_out=po_ref, pair_sqnorm=sq_ref)
-    po = torch.empty((n, H), dtype=torch.float32, device="cuda")
+                              r.sorted_pair_ids, r.topk_w, pair_out=po_ref, pair_scale=ps_ref, pair_sqnorm=sq_ref)
+    po = torch.empty((n, H), dtype=torch.float16, device="cuda")
+    ps = torch.empty((n,), dtype=torch.float32, device="cuda")
     sq = torch.empty((n,), dtype=torch.float32, device="cuda")
     args = (xc, xs, layer.x_gs, *layer.w13, *layer.w2, layer.h_gs, case.k, r.expert_offsets, r.sorted_pair_ids,
-            r.topk_w, po, sq)
+            r.topk_w, po, ps, sq)
     ops.moe_nvfp4_grouped_ffn_noalloc(*args)  # eager: the per-device set-up happens outside the capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -73,9 +80,11 @@ def test_noalloc_captured_in_a_graph(ops):
     torch.cuda.synchronize()
     for rep in range(3):
         po.fill_(float("nan"))
+        ps.fill_(float("nan"))
         sq.fill_(float("nan"))
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(po, po_ref), f"replay {rep}: pair_out differs"
+        assert torch.equal(ps, ps_ref), f"replay {rep}: pair_scale differs"
         assert torch.equal(sq, sq_ref), f"replay {rep}: pair_sqnorm differs"
