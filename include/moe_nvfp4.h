@@ -81,7 +81,8 @@
 extern "C" {
 #endif
 
-#define MOE_NVFP4_ABI_VERSION 2
+/* 3: pair rows FP16 with a per-row pair_scale (2: tiled weight block scales) */
+#define MOE_NVFP4_ABI_VERSION 3
 
 typedef int32_t moe_status;
 #define MOE_OK 0

@@ -18,6 +18,7 @@ LIB_PATH = os.environ.get("MOE_NVFP4_LIB") or os.path.join(os.path.dirname(os.pa
                                                            "libmoe_nvfp4.so")
 
 MOE_OK = 0
+ABI_VERSION = 3  # MOE_NVFP4_ABI_VERSION these signatures follow
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_WORKSPACE",
                 5: "MOE_ERR_DEVICE", 6: "MOE_ERR_LAUNCH"}
 
@@ -78,6 +79,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    version = lib.moe_abi_version()
+    if version != ABI_VERSION:
+        raise RuntimeError(f"{path} implements ABI version {version}, this binding expects {ABI_VERSION}; rebuild it")
     return lib
 
 

@@ -47,7 +47,7 @@ def test_binding_signatures_cover_header():
 
 
 def test_version(L):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def _route(L, x=P, T=4, H=64, ldx=64, wr=P, bias=P, E=8, k=2, rsf=2.5, ws=P2, wsb=1 << 20):

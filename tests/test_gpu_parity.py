@@ -40,7 +40,7 @@ def ops():
 def test_library_loaded_in_tree(ops):
     path = ops.lib()._name
     assert os.path.exists(path) and "nvfp4_w4a4_mixture_amd" in path
-    assert ops.lib().moe_abi_version() == 2
+    assert ops.lib().moe_abi_version() == 3
 
 
 # ---------------------------------------------------------------------------
