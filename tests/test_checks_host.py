@@ -64,3 +64,33 @@ def test_invalid_choices_are_rejected(mutation):
         ref["gap"][1] = 1.0
     with pytest.raises(AssertionError):
         check_routing(g_ids, g_w, ref, 2.5, E, *args)
+
+
+def test_expected_pair_scale_rule():
+    """The row-scale rule the GPU pair rows are checked against: 2^E with B * 2^-E in [2^14, 2^15) for every bound
+    in FP32's normal range not clamped, so the largest value any FP4 operands allow stays below FP16's 65504; the
+    exponent clamps at -126 and 113; the scale is a power of two."""
+    from gpu_cases import expected_pair_scale
+
+    rng = np.random.default_rng(5)
+    n = 20000
+    w = rng.uniform(0.0, 3.0, n).astype(np.float32)
+    w[:5] = [0.0, 1e-30, 2.5, np.float32(2.0 ** -126), 1.0]
+    ids = rng.integers(0, 4, n)
+    h_gs = np.float32(10.0) ** rng.uniform(-3, 12, 4).astype(np.float32)
+    w2_gs = np.float32(10.0) ** rng.uniform(-3, 6, 4).astype(np.float32)
+    I = 2048
+    sc = expected_pair_scale(w, ids, I, h_gs, w2_gs)
+    m, e = np.frexp(sc)
+    assert np.all(m == 0.5)  # powers of two
+    E = e.astype(np.int64) - 1
+    assert E.min() >= -126 and E.max() <= 113
+    bound = (w.astype(np.float64) * I * 2688.0 ** 2) / (h_gs[ids].astype(np.float64) * w2_gs[ids].astype(np.float64))
+    scaled = bound * np.ldexp(1.0, -E)
+    free = (E > -126) & (E < 113)
+    assert np.all(scaled[free] < 2.0 ** 15 * (1 + 1e-6)) and np.all(scaled[free] >= 2.0 ** 14 * (1 - 1e-6))
+    assert np.all(scaled < 2.0 ** 15 * (1 + 1e-6))  # clamped at the bottom: smaller still
+    assert np.all(E[w == 0] == -126)
+    # an FP16 value below 2^15 times the scale is exact in FP32, as the combine relies on
+    big = np.float16(32752.0).astype(np.float32) * sc  # largest FP16 below 2^15
+    assert np.all(np.isfinite(big))
