@@ -50,8 +50,9 @@
  *  Pair rows  The weighted expert output of pair p, w_p * f, as FP16 values
  *             pair_out [T*k, H] (IEEE binary16 bits) times a power of two
  *             pair_scale [T*k] (FP32): value = fp16(pair_out[p, c]) *
- *             pair_scale[p], which is exact in FP32.  pair_scale[p] = 2^E with
- *             E = floor(log2(B)) - 14, clamped to [-126, 113], for the bound
+ *             pair_scale[p], which is exact in FP32 (above FP32's subnormal
+ *             range).  pair_scale[p] = 2^E with E = floor(log2(B)) - 14,
+ *             clamped to [-126, 113], for the bound, with e the expert of pair p,
  *             B = |w_p| * (I * 2688^2) * (1 / (h_gs[e] * w2_gs[e])) (FP32
  *             operations in that order) that no FP4 operands can exceed
  *             (2688 = 6 * 448, the largest decoded element); every stored
