@@ -286,6 +286,16 @@ def _layer_check(ops, case, reap=True):
     ps = to_np(out32.pair_scale)
     assert np.array_equal(ps, expected_pair_scale(w, ids, case.I, to_np(layer.h_gs), to_np(layer.w2[2])))
     assert float(out32.pair_out.abs().max()) < 2.0 ** 15
+    # and they are rounded to nearest: within half an FP16 ulp of the oracle's value over the row scale, up to the
+    # FP32-against-FP64 difference of f (1e-5 relative); a truncating or double-rounding encoder would miss about
+    # half the elements.  Rows whose h codes sit on the other side of a rounding boundary (rare) are in the 1%.
+    ref_s = pair_ref / ps.astype(np.float64)[:, None]
+    got_s = to_np(out32.pair_out).astype(np.float64)
+    e2 = np.floor(np.log2(np.maximum(np.abs(ref_s), 2.0 ** -24))).astype(np.int64)  # binade of the value
+    ulp = np.ldexp(1.0, np.maximum(e2, -14) - 10)
+    rounded = np.abs(got_s - ref_s) <= 0.5 * ulp + 1e-5 * np.abs(ref_s)
+    print(f"  pair values within half an FP16 ulp: {rounded.mean():.6f}", flush=True)
+    assert rounded.mean() >= 0.99
     if reap:
         sal = to_np(out32.saliency).astype(np.float64)
         cnt = np.bincount(ids.reshape(-1), minlength=case.E)
